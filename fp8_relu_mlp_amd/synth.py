@@ -1,0 +1,101 @@
+"""Seeded synthetic inputs for the MLP path (shared by tests, smoke and bench).
+
+This module only draws random numbers and stores them as bf16 bit patterns.
+It holds none of the method's arithmetic, imports nothing from the library
+binding and nothing from the CPU oracle, so both sides can be fed the very
+same bits.
+
+Stand-in workload: the speedrun pages train a GPT-2-small tier model
+(model width 768, ReLU^2 MLP with hidden width 4*768) on FineWeb tokens.  No
+dataset is used here; activations are drawn as post-RMSNorm-like N(0, 1) rows
+and weights with fan-in variance, the shapes of that model's MLP block and
+attention projections.  N(mu, v) always names the variance v.
+
+Every tensor has its own stream: ``numpy.random.default_rng`` seeded with
+(seed, crc32(name)), so adding a tensor never shifts another one's values.
+Draws are float64, rounded to fp32 by numpy and to bf16 by torch's CPU cast
+(round-to-nearest-even); the resulting bit patterns are the inputs.
+"""
+import zlib
+
+import numpy as np
+import torch
+
+WORKLOADS = {
+    # name: (M, d, h, seed)
+    "tiny": (256, 128, 512, 0),           # one forward step, exact amax as amax_prev
+    "fwd2": (16384, 768, 3072, 1),        # two forward steps, delayed scale
+    "fwdbwd": (49152, 768, 3072, 2),      # forward + backward, the timed workload
+    "stack": (65536, 768, 3072, 4),       # 12 layers x 8 steps with state carry
+}
+ATTN = {"M": 49152, "d": 768, "qkv": 2304, "seed": 3}
+
+
+def rng(seed, name):
+    return np.random.default_rng([int(seed), zlib.crc32(name.encode())])
+
+
+def to_bf16_bits(x):
+    """float array -> uint16 bf16 bit patterns via torch's CPU cast."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def normal_bf16(shape, var, seed, name):
+    """bf16 bits of N(0, var) draws for one named tensor."""
+    g = rng(seed, name)
+    x = g.standard_normal(size=shape) * np.sqrt(var)
+    return to_bf16_bits(x)
+
+
+def ternary_bf16(shape, seed, name, nnz_per_row=None):
+    """bf16 bits of values in {-1, 0, +1}; with nnz_per_row, each row has at
+    most that many non-zeros (used for the lossless special case)."""
+    g = rng(seed, name)
+    if nnz_per_row is None:
+        x = g.integers(-1, 2, size=shape).astype(np.float64)
+    else:
+        x = np.zeros(shape)
+        for r in range(shape[0]):
+            cols = g.choice(shape[1], size=nnz_per_row, replace=False)
+            x[r, cols] = g.choice([-1.0, 1.0], size=nnz_per_row)
+    return to_bf16_bits(x)
+
+
+def mlp_inputs(M, d, h, seed, with_dy=False, step=0):
+    """X [M,d] ~ N(0,1); W1 [h,d] ~ N(0,1/d); W2 [d,h] ~ N(0,1/h);
+    dY [M,d] ~ N(0,1e-3) when requested.  ``step`` selects a fresh X/dY."""
+    out = {
+        "X": normal_bf16((M, d), 1.0, seed, f"X.{step}"),
+        "W1": normal_bf16((h, d), 1.0 / d, seed, "W1"),
+        "W2": normal_bf16((d, h), 1.0 / h, seed, "W2"),
+    }
+    if with_dy:
+        out["dY"] = normal_bf16((M, d), 1e-3, seed, f"dY.{step}")
+    return out
+
+
+def perturbed_w1(W1_bits, seed):
+    """Step-2 weights of the two-step forward workload: W1 + 1e-3 * N(0, 1/d),
+    added in fp32 and rounded back to bf16 (a new input, not part of the path)."""
+    h, d = W1_bits.shape
+    g = rng(seed, "W1.delta")
+    delta = (1e-3 * g.standard_normal(size=(h, d)) * np.sqrt(1.0 / d)).astype(np.float32)
+    w = torch.from_numpy(W1_bits.view(np.int16).copy()).view(torch.bfloat16).float()
+    w = w + torch.from_numpy(delta)
+    return w.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def attn_inputs(M=None, d=None, qkv=None, seed=None):
+    """FP8 attention projection workload: X [M,d] ~ N(0,1), Wqkv [qkv,d] and
+    Wo [d,d] ~ N(0,1/d), O-projection input Xo [M,d] ~ N(0,0.5)."""
+    M = ATTN["M"] if M is None else M
+    d = ATTN["d"] if d is None else d
+    qkv = ATTN["qkv"] if qkv is None else qkv
+    seed = ATTN["seed"] if seed is None else seed
+    return {
+        "X": normal_bf16((M, d), 1.0, seed, "X"),
+        "Wqkv": normal_bf16((qkv, d), 1.0 / d, seed, "Wqkv"),
+        "Xo": normal_bf16((M, d), 0.5, seed, "Xo"),
+        "Wo": normal_bf16((d, d), 1.0 / d, seed, "Wo"),
+    }
