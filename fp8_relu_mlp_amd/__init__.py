@@ -1,0 +1,181 @@
+"""Fused FP8 ReLU^2 MLP for AMD Instinct MI355X (gfx950).
+
+Python binding of libfp8mlp (include/fp8mlp.h).  The functions below only
+marshal torch tensors (device pointers, sizes, the current HIP stream) into
+the C ABI; every step of the computation runs in the library's HIP kernels.
+PyTorch supplies device memory and streams and nothing else.  If the library
+is not built, the first call raises.
+
+Entry points (same names as the C ABI):
+  mlp_relu2_fwd, mlp_relu2_bwd, fp8_cast_transpose, fp8_cast_transpose_w2,
+  amax_reduce, fp8_scale_from_amax, fp8_linear
+and ``Relu2MLP``, one MLP block's device state (bf16 weights, the transposed
+fp8 W2 cache with its scales, the delayed-scale amax carried between steps).
+"""
+import torch
+
+from ._lib import Fp8MlpError, check, lib  # noqa: F401
+
+TRAIN_FP8 = 0
+EVAL_BF16 = 1
+F32 = 0
+BF16 = 1
+
+__all__ = ["mlp_relu2_fwd", "mlp_relu2_bwd", "fp8_cast_transpose", "fp8_cast_transpose_w2", "amax_reduce",
+           "fp8_scale_from_amax", "fp8_linear", "Relu2MLP", "Fp8MlpError", "TRAIN_FP8", "EVAL_BF16"]
+
+
+def _p(t):
+    """Device pointer of a tensor (or NULL for None)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("fp8mlp tensors must live in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError("fp8mlp tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ws(nbytes, workspace, device):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def mlp_relu2_fwd(mode, X, W1, W2t_q, w2_inv_scale, W2, amax_prev, margin, post, post_q, amax_out, scale_out, Y,
+                  workspace=None, stream=None):
+    """See mlp_relu2_fwd in include/fp8mlp.h.  X [M,d] bf16, W1 [h,d] bf16,
+    W2t_q [h,d] uint8, W2 [d,h] bf16, post [M,h] bf16, post_q [M,h] uint8,
+    Y [M,d] bf16; scalars are 1-element fp32 device tensors."""
+    M, d = X.shape
+    h = W1.shape[0]
+    L = lib()
+    ws, wsb = _ws(L.mlp_relu2_fwd_workspace(M, d, h), workspace, X.device)
+    check("mlp_relu2_fwd", L.mlp_relu2_fwd(
+        mode, _p(X), _p(W1), _p(W2t_q), _p(w2_inv_scale), _p(W2), _p(amax_prev), float(margin), _p(post),
+        _p(post_q), _p(amax_out), _p(scale_out), _p(Y), M, d, h, _p(ws), wsb, _stream(stream)))
+
+
+def mlp_relu2_bwd(dY, X, W1, W2, post, dX, dW1, dW2, accumulate=False, workspace=None, stream=None):
+    """See mlp_relu2_bwd in include/fp8mlp.h.  dW1 [h,d], dW2 [d,h] fp32."""
+    M, d = X.shape
+    h = W1.shape[0]
+    L = lib()
+    ws, wsb = _ws(L.mlp_relu2_bwd_workspace(M, d, h), workspace, X.device)
+    check("mlp_relu2_bwd", L.mlp_relu2_bwd(
+        _p(dY), _p(X), _p(W1), _p(W2), _p(post), _p(dX), _p(dW1), _p(dW2), int(bool(accumulate)), M, d, h,
+        _p(ws), wsb, _stream(stream)))
+
+
+def fp8_cast_transpose(W, Wt_q, scale_in=None, scale_out=None, inv_scale_out=None, amax_out=None,
+                       workspace=None, stream=None):
+    """bf16 W [N,K] -> e4m3 Wt_q [K,N] (uint8); see include/fp8mlp.h."""
+    N, K = W.shape
+    L = lib()
+    ws, wsb = _ws(L.fp8_cast_transpose_workspace(N, K), workspace, W.device)
+    check("fp8_cast_transpose", L.fp8_cast_transpose(
+        _p(W), N, K, _p(Wt_q), _p(scale_in), _p(scale_out), _p(inv_scale_out), _p(amax_out), _p(ws), wsb,
+        _stream(stream)))
+
+
+def fp8_cast_transpose_w2(W2, W2t_q, scale_out=None, inv_scale_out=None, amax_out=None, workspace=None,
+                          stream=None):
+    """Exact refresh of the transposed fp8 W2 cache: W2 [d,h] -> W2t_q [h,d]."""
+    d, h = W2.shape
+    L = lib()
+    ws, wsb = _ws(L.fp8_cast_transpose_workspace(d, h), workspace, W2.device)
+    check("fp8_cast_transpose_w2", L.fp8_cast_transpose_w2(
+        _p(W2), d, h, _p(W2t_q), _p(scale_out), _p(inv_scale_out), _p(amax_out), _p(ws), wsb,
+        _stream(stream)))
+
+
+def amax_reduce(x, amax_out, workspace=None, stream=None):
+    """amax_out = max |x| for an fp32 or bf16 tensor."""
+    if x.dtype == torch.float32:
+        dt = F32
+    elif x.dtype == torch.bfloat16:
+        dt = BF16
+    else:
+        raise ValueError("amax_reduce takes float32 or bfloat16")
+    n = x.numel()
+    L = lib()
+    ws, wsb = _ws(L.amax_reduce_workspace(n), workspace, x.device)
+    check("amax_reduce", L.amax_reduce(dt, _p(x) if n else None, n, _p(amax_out), _p(ws), wsb, _stream(stream)))
+
+
+def fp8_scale_from_amax(amax, margin, scale_out=None, inv_scale_out=None, stream=None):
+    """scale = 448 / (margin * amax) on the device (1 if not positive finite)."""
+    check("fp8_scale_from_amax", lib().fp8_scale_from_amax(
+        _p(amax), float(margin), _p(scale_out), _p(inv_scale_out), _stream(stream)))
+
+
+def fp8_linear(X, x_scale, Wt_q, w_inv_scale, Y, x_amax_out=None, stream=None):
+    """Y [M,N] = FP8 linear of X [M,K] bf16 with Wt_q [K,N] e4m3."""
+    M, K = X.shape
+    N = Wt_q.shape[1]
+    check("fp8_linear", lib().fp8_linear(
+        _p(X), _p(x_scale), _p(Wt_q), _p(w_inv_scale), _p(Y), _p(x_amax_out), M, K, N, _stream(stream)))
+
+
+class Relu2MLP:
+    """Device state of one MLP block for delayed-scale FP8 training.
+
+    Holds the bf16 master weights W1 [h,d] and W2 [d,h], the transposed e4m3
+    W2 cache W2t_q [h,d] with its scale / inverse scale / amax (refreshed by
+    ``refresh_w2_cache`` after every weight update), and the activation amax
+    of the previous step (``amax_prev``), which the next forward turns into
+    its quantisation scale.  Carrying the state is a buffer swap: the amax a
+    forward writes becomes the next forward's ``amax_prev``.
+    """
+
+    def __init__(self, W1, W2, margin=2.0, amax_init=None):
+        dev = W1.device
+        self.W1, self.W2, self.margin = W1, W2, float(margin)
+        h, d = W1.shape
+        self.d, self.h = d, h
+        f = lambda: torch.zeros(1, dtype=torch.float32, device=dev)
+        self.w2_scale, self.w2_inv_scale, self.w2_amax = f(), f(), f()
+        self.W2t_q = torch.empty((h, d), dtype=torch.uint8, device=dev)
+        self.amax_prev, self._amax_next, self.scale_used = f(), f(), f()
+        if amax_init is not None:
+            self.amax_prev.fill_(float(amax_init))
+        self.refresh_w2_cache()
+
+    def refresh_w2_cache(self, stream=None):
+        fp8_cast_transpose_w2(self.W2, self.W2t_q, self.w2_scale, self.w2_inv_scale, self.w2_amax, stream=stream)
+
+    def forward(self, X, mode=TRAIN_FP8, post=None, post_q=None, Y=None, carry=True, stream=None):
+        """Returns (Y, post, post_q).  With carry, the amax measured here
+        becomes amax_prev for the next call."""
+        M = X.shape[0]
+        dev = X.device
+        post = torch.empty((M, self.h), dtype=torch.bfloat16, device=dev) if post is None else post
+        if mode == TRAIN_FP8 and post_q is None:
+            post_q = torch.empty((M, self.h), dtype=torch.uint8, device=dev)
+        Y = torch.empty((M, self.d), dtype=torch.bfloat16, device=dev) if Y is None else Y
+        mlp_relu2_fwd(mode, X, self.W1, self.W2t_q, self.w2_inv_scale, self.W2, self.amax_prev, self.margin,
+                      post, post_q if mode == TRAIN_FP8 else None, self._amax_next,
+                      self.scale_used if mode == TRAIN_FP8 else None, Y, stream=stream)
+        if carry:
+            self.amax_prev, self._amax_next = self._amax_next, self.amax_prev
+        return Y, post, post_q
+
+    @property
+    def amax_last(self):
+        """The amax measured by the most recent carried forward."""
+        return self.amax_prev
+
+    def backward(self, dY, X, post, dX=None, dW1=None, dW2=None, accumulate=False, stream=None):
+        dev = X.device
+        dX = torch.empty_like(X) if dX is None else dX
+        dW1 = torch.empty((self.h, self.d), dtype=torch.float32, device=dev) if dW1 is None else dW1
+        dW2 = torch.empty((self.d, self.h), dtype=torch.float32, device=dev) if dW2 is None else dW2
+        mlp_relu2_bwd(dY, X, self.W1, self.W2, post, dX, dW1, dW2, accumulate, stream=stream)
+        return dX, dW1, dW2

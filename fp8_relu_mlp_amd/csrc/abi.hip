@@ -1,0 +1,281 @@
+// libfp8mlp: status / version / device check, the amax reduction, the scale
+// computation and the FP8 weight cast-transpose.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "common.h"
+#include "host.h"
+
+namespace fp8mlp {
+
+thread_local int g_last_hip_error = 0;
+
+// ------------------------------------------------------------------ device check
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+}  // namespace
+
+int check_device() {
+  int dev = 0;
+  FP8MLP_TRY(hip_status(hipGetDevice(&dev)));
+  if (dev < 0 || dev >= kMaxDevices) return FP8MLP_E_ARCH;
+  int st = g_dev_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    FP8MLP_TRY(hip_status(hipGetDeviceProperties(&prop, dev)));
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? FP8MLP_OK : FP8MLP_E_ARCH;
+}
+
+// ------------------------------------------------------------------ amax
+// Maximum of |x| taken on bit patterns: for fp32, |x| bits order like the
+// values (+0 < ... < +inf < NaN), so the unsigned maximum is exact, NaN
+// propagating and independent of the reduction order.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+  v = wave_max_u32(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  uint32_t m = 0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); i++) m = red[i] > m ? red[i] : m;
+  return m;
+}
+
+template <int DT>
+__global__ void __launch_bounds__(256) k_amax_partial(const void* __restrict__ x, int64_t n,
+                                                      uint32_t* __restrict__ partial) {
+  __shared__ uint32_t red[4];
+  uint32_t m = 0;
+  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  constexpr int PER = DT == FP8MLP_F32 ? 4 : 8;  // elements per 16-byte vector
+  const int64_t nv = n / PER;
+  const i32x4* v = (const i32x4*)x;
+  for (int64_t i = tid; i < nv; i += stride) {
+    const i32x4 q = __builtin_nontemporal_load(v + i);
+    const uint32_t w[4] = {(uint32_t)q[0], (uint32_t)q[1], (uint32_t)q[2], (uint32_t)q[3]};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      if constexpr (DT == FP8MLP_F32) {
+        uint32_t a = w[j] & 0x7fffffffu;
+        m = a > m ? a : m;
+      } else {
+        uint32_t a0 = (w[j] & 0x7fffu) << 16, a1 = (w[j] >> 16 & 0x7fffu) << 16;
+        m = a0 > m ? a0 : m;
+        m = a1 > m ? a1 : m;
+      }
+    }
+  }
+  for (int64_t i = nv * PER + tid; i < n; i += stride) {
+    uint32_t a;
+    if constexpr (DT == FP8MLP_F32) a = ((const uint32_t*)x)[i] & 0x7fffffffu;
+    else a = (uint32_t)(((const uint16_t*)x)[i] & 0x7fffu) << 16;
+    m = a > m ? a : m;
+  }
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+// One block: max over n unsigned |x| bit patterns -> out (as fp32).
+// Optionally writes the delayed scale computed from *amax_prev and margin.
+__global__ void __launch_bounds__(256) k_max_final(const uint32_t* __restrict__ bits, int64_t n, float* out,
+                                                   const float* amax_prev, float margin, float* scale_out) {
+  __shared__ uint32_t red[4];
+  uint32_t m = 0;
+  for (int64_t i = threadIdx.x; i < n; i += 256) {
+    uint32_t a = bits[i] & 0x7fffffffu;
+    m = a > m ? a : m;
+  }
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) {
+    *out = __uint_as_float(m);
+    if (scale_out) *scale_out = scale_from_amax(*amax_prev, margin);
+  }
+}
+
+// Direct single-block amax of a small tensor.
+template <int DT>
+__global__ void __launch_bounds__(256) k_amax_small(const void* __restrict__ x, int64_t n, float* out) {
+  __shared__ uint32_t red[4];
+  uint32_t m = 0;
+  for (int64_t i = threadIdx.x; i < n; i += 256) {
+    uint32_t a;
+    if constexpr (DT == FP8MLP_F32) a = ((const uint32_t*)x)[i] & 0x7fffffffu;
+    else a = (uint32_t)(((const uint16_t*)x)[i] & 0x7fffu) << 16;
+    m = a > m ? a : m;
+  }
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) *out = __uint_as_float(m);
+}
+
+constexpr int64_t kAmaxSmall = 1 << 16;
+constexpr int kAmaxBlocks = 2048;
+
+size_t amax_ws_bytes(int64_t n) { return n <= kAmaxSmall ? 0 : (size_t)kAmaxBlocks * 4; }
+
+int launch_max_small(const float* x, int64_t n, float* out, const float* amax_prev, float margin,
+                     float* scale_out, hipStream_t stream) {
+  hipLaunchKernelGGL(k_max_final, dim3(1), dim3(256), 0, stream, (const uint32_t*)x, n, out, amax_prev, margin,
+                     scale_out);
+  return launch_status();
+}
+
+int launch_amax(int dtype, const void* x, int64_t n, float* out, void* workspace, size_t ws_bytes,
+                hipStream_t stream) {
+  if (n <= kAmaxSmall) {
+    if (dtype == FP8MLP_F32)
+      hipLaunchKernelGGL(k_amax_small<FP8MLP_F32>, dim3(1), dim3(256), 0, stream, x, n, out);
+    else
+      hipLaunchKernelGGL(k_amax_small<FP8MLP_BF16>, dim3(1), dim3(256), 0, stream, x, n, out);
+    return launch_status();
+  }
+  const int per = dtype == FP8MLP_F32 ? 4 : 8;
+  int64_t blocks = cdiv(cdiv(n, per), 256 * 4);
+  if (blocks > kAmaxBlocks) blocks = kAmaxBlocks;
+  uint32_t* partial = (uint32_t*)workspace;
+  if (dtype == FP8MLP_F32)
+    hipLaunchKernelGGL(k_amax_partial<FP8MLP_F32>, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, partial);
+  else
+    hipLaunchKernelGGL(k_amax_partial<FP8MLP_BF16>, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, partial);
+  FP8MLP_TRY(launch_status());
+  hipLaunchKernelGGL(k_max_final, dim3(1), dim3(256), 0, stream, (const uint32_t*)partial, blocks, out,
+                     (const float*)nullptr, 0.0f, (float*)nullptr);
+  return launch_status();
+}
+
+// ------------------------------------------------------------------ scale
+__global__ void k_scale_from_amax(const float* amax, float margin, float* scale_out, float* inv_out) {
+  const float s = scale_from_amax(*amax, margin);
+  if (scale_out) *scale_out = s;
+  if (inv_out) *inv_out = 1.0f / s;
+}
+
+// ------------------------------------------------------------------ cast-transpose
+// bf16 W [N, K] -> e4m3 Wt [K, N] through a 64 x 64 LDS tile.  The scale is
+// read from scale_in, or computed as 448 / amax (exact policy).
+__global__ void __launch_bounds__(256) k_cast_transpose(const uint16_t* __restrict__ W, int64_t N, int64_t K,
+                                                        uint8_t* __restrict__ Wt, const float* scale_in,
+                                                        const float* amax_in, float* scale_out, float* inv_out,
+                                                        float* amax_out) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[64][80];  // [k][n]
+  const float s = scale_in ? *scale_in : scale_from_amax(*amax_in, 1.0f);
+  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
+#pragma unroll
+  for (int it = 0; it < 2; it++) {
+    const int c = threadIdx.x + it * 256;
+    const int r = c >> 3, ch = c & 7;
+    const int64_t n = n0 + r, k = k0 + ch * 8;
+    if (n < N && k < K) {
+      const uint4 v = *(const uint4*)(W + n * K + k);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t lo = pack_e4m3x4(bf16_lo(w[0]) * s, bf16_hi(w[0]) * s, bf16_lo(w[1]) * s, bf16_hi(w[1]) * s);
+      const uint32_t hi = pack_e4m3x4(bf16_lo(w[2]) * s, bf16_hi(w[2]) * s, bf16_lo(w[3]) * s, bf16_hi(w[3]) * s);
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        tile[ch * 8 + e][r] = (uint8_t)(lo >> (8 * e));
+        tile[ch * 8 + 4 + e][r] = (uint8_t)(hi >> (8 * e));
+      }
+    }
+  }
+  __syncthreads();
+  {
+    const int r = threadIdx.x >> 2, ch = threadIdx.x & 3;
+    const int64_t k = k0 + r, n = n0 + ch * 16;
+    if (k < K && n < N) *(uint4*)(Wt + k * N + n) = *(const uint4*)&tile[r][ch * 16];
+  }
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    if (scale_out) *scale_out = s;
+    if (inv_out) *inv_out = 1.0f / s;
+    if (amax_out) *amax_out = amax_in ? *amax_in : 0.0f;
+  }
+}
+
+}  // namespace fp8mlp
+
+using namespace fp8mlp;
+
+extern "C" {
+
+int fp8mlp_abi_version(void) { return FP8MLP_ABI_VERSION; }
+
+const char* fp8mlp_status_str(int status) {
+  switch (status) {
+    case FP8MLP_OK: return "ok";
+    case FP8MLP_E_NULL: return "a required pointer is NULL";
+    case FP8MLP_E_SHAPE: return "invalid size (negative, zero where not allowed, or not a multiple of 64)";
+    case FP8MLP_E_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case FP8MLP_E_WORKSPACE: return "workspace missing or too small";
+    case FP8MLP_E_ARCH: return "the current device is not gfx950 (MI355X)";
+    case FP8MLP_E_HIP: return "a HIP call failed";
+    case FP8MLP_E_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+int fp8mlp_last_hip_error(void) { return g_last_hip_error; }
+
+size_t amax_reduce_workspace(int64_t n) { return n < 0 ? 0 : amax_ws_bytes(n); }
+
+int amax_reduce(int dtype, const void* x, int64_t n, float* amax_out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  FP8MLP_REQUIRE(dtype == FP8MLP_F32 || dtype == FP8MLP_BF16, FP8MLP_E_ARG);
+  FP8MLP_REQUIRE(n >= 0, FP8MLP_E_SHAPE);
+  FP8MLP_REQUIRE(amax_out && (x || n == 0), FP8MLP_E_NULL);
+  FP8MLP_REQUIRE((x == nullptr || aligned16(x)) && ((uintptr_t)amax_out & 3) == 0, FP8MLP_E_ALIGN);
+  const size_t need = amax_ws_bytes(n);
+  FP8MLP_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), FP8MLP_E_WORKSPACE);
+  FP8MLP_REQUIRE(need == 0 || aligned16(workspace), FP8MLP_E_ALIGN);
+  FP8MLP_TRY(check_device());
+  return launch_amax(dtype, x, n, amax_out, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int fp8_scale_from_amax(const float* amax, float margin, float* scale_out, float* inv_scale_out, void* stream) {
+  FP8MLP_REQUIRE(amax != nullptr, FP8MLP_E_NULL);
+  FP8MLP_REQUIRE(margin > 0.0f && margin <= 3.4e38f, FP8MLP_E_ARG);
+  FP8MLP_TRY(check_device());
+  hipLaunchKernelGGL(k_scale_from_amax, dim3(1), dim3(1), 0, (hipStream_t)stream, amax, margin, scale_out,
+                     inv_scale_out);
+  return launch_status();
+}
+
+size_t fp8_cast_transpose_workspace(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return 256 + amax_ws_bytes(N * K);
+}
+
+int fp8_cast_transpose(const uint16_t* W, int64_t N, int64_t K, uint8_t* Wt_q, const float* scale_in,
+                       float* scale_out, float* inv_scale_out, float* amax_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  FP8MLP_REQUIRE(N > 0 && K > 0 && N % 16 == 0 && K % 16 == 0, FP8MLP_E_SHAPE);
+  FP8MLP_REQUIRE(W && Wt_q, FP8MLP_E_NULL);
+  FP8MLP_REQUIRE(aligned16(W) && aligned16(Wt_q), FP8MLP_E_ALIGN);
+  const bool need_amax = scale_in == nullptr || amax_out != nullptr;
+  const size_t need = need_amax ? fp8_cast_transpose_workspace(N, K) : 0;
+  FP8MLP_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), FP8MLP_E_WORKSPACE);
+  FP8MLP_REQUIRE(need == 0 || aligned16(workspace), FP8MLP_E_ALIGN);
+  FP8MLP_TRY(check_device());
+  hipStream_t st = (hipStream_t)stream;
+  float* amax_slot = nullptr;
+  if (need_amax) {
+    amax_slot = (float*)workspace;
+    FP8MLP_TRY(launch_amax(FP8MLP_BF16, W, N * K, amax_slot, (char*)workspace + 256, workspace_bytes - 256, st));
+  }
+  dim3 grid((unsigned)cdiv(K, 64), (unsigned)cdiv(N, 64));
+  hipLaunchKernelGGL(k_cast_transpose, grid, dim3(256), 0, st, W, N, K, Wt_q, scale_in, (const float*)amax_slot,
+                     scale_out, inv_scale_out, amax_out);
+  return launch_status();
+}
+
+int fp8_cast_transpose_w2(const uint16_t* W2, int64_t d, int64_t h, uint8_t* W2t_q, float* scale_out,
+                          float* inv_scale_out, float* amax_out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return fp8_cast_transpose(W2, d, h, W2t_q, nullptr, scale_out, inv_scale_out, amax_out, workspace,
+                            workspace_bytes, stream);
+}
+
+}  // extern "C"

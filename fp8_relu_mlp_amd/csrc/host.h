@@ -1,0 +1,52 @@
+// Host-side helpers of libfp8mlp: status handling, argument validation,
+// device architecture check and launch error capture.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/fp8mlp.h"
+
+namespace fp8mlp {
+
+// hipError_t of the last failed HIP call on this thread.
+extern thread_local int g_last_hip_error;
+
+// FP8MLP_OK when the current device is gfx950, FP8MLP_E_ARCH otherwise,
+// FP8MLP_E_HIP if the device cannot be queried.  Cached per device.
+int check_device();
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline int hip_status(hipError_t e) {
+  if (e == hipSuccess) return FP8MLP_OK;
+  g_last_hip_error = (int)e;
+  return FP8MLP_E_HIP;
+}
+// Status of the most recent kernel launch on this thread.
+inline int launch_status() { return hip_status(hipGetLastError()); }
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+#define FP8MLP_TRY(expr)                 \
+  do {                                   \
+    int _st = (expr);                    \
+    if (_st != FP8MLP_OK) return _st;    \
+  } while (0)
+#define FP8MLP_REQUIRE(cond, status)     \
+  do {                                   \
+    if (!(cond)) return (status);        \
+  } while (0)
+
+// Shared launchers (defined in abi.hip) used by several entry points.
+// Reduce n fp32 values that are >= +0 or NaN to their maximum, written to
+// out (and, if scale_out is given, the delayed scale from amax_prev/margin).
+int launch_max_small(const float* x, int64_t n, float* out, const float* amax_prev, float margin,
+                     float* scale_out, hipStream_t stream);
+int launch_amax(int dtype, const void* x, int64_t n, float* out, void* workspace, size_t ws_bytes,
+                hipStream_t stream);
+size_t amax_ws_bytes(int64_t n);
+
+}  // namespace fp8mlp

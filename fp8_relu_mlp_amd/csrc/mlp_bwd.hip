@@ -1,0 +1,148 @@
+// mlp_relu2_bwd: the bf16 backward of the ReLU^2 MLP block.
+//   dpost = dY W2            fused epilogue: dpre = bf16(2 sqrt(post) dpost)
+//   dX    = dpre W1          bf16 out
+//   dW1   = dpre^T X         fp32, split-k over M, reduced in split order
+//   dW2   = dY^T post        fp32, split-k over M, reduced in split order
+#include "launch.h"
+
+namespace fp8mlp {
+
+// dY [M,d] . W2 [d,h]: W2 is k-major here, read with transposing LDS loads.
+using CfgDpost = GemmCfg<2, 256, 256, 2, KC, MNC>;
+// dpre [M,h] . W1 [h,d]
+using CfgDx = GemmCfg<2, 192, 256, 2, KC, MNC>;
+// dpre^T . X and dY^T . post: both operands are row-contiguous with k = token.
+using CfgDw = GemmCfg<2, 256, 256, 2, MNC, MNC>;
+
+struct BwdPlan {
+  size_t dpre_bytes, part_bytes;
+  int splits;
+  int64_t k_per_split;
+};
+
+static BwdPlan bwd_plan(int64_t M, int64_t d, int64_t h) {
+  BwdPlan p;
+  p.dpre_bytes = align_up((size_t)(M * h) * 2, 256);
+  const int64_t tiles = cdiv(h, CfgDw::BM) * cdiv(d, CfgDw::BN);
+  int64_t s = 256 / (tiles > 0 ? tiles : 1);
+  const int64_t max_s = cdiv(M, 512);
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  p.k_per_split = cdiv(cdiv(M, s), 64) * 64;
+  if (p.k_per_split == 0) p.k_per_split = 64;
+  p.splits = (int)(M > 0 ? cdiv(M, p.k_per_split) : 1);
+  p.part_bytes = p.splits > 1 ? align_up((size_t)p.splits * (size_t)(h * d) * 4, 256) : 0;
+  return p;
+}
+
+// out[i] = (accumulate ? out[i] : 0) + part[0][i] + part[1][i] + ... in split order.
+__global__ void __launch_bounds__(256) k_splitk_reduce(const float4* __restrict__ part, int splits, int64_t n4,
+                                                       float4* __restrict__ out, int accumulate) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    float4 a = accumulate ? out[i] : float4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < splits; s++) {
+      const float4 v = part[s * n4 + i];
+      a.x += v.x;
+      a.y += v.y;
+      a.z += v.z;
+      a.w += v.w;
+    }
+    out[i] = a;
+  }
+}
+
+__global__ void __launch_bounds__(256) k_fill_zero(float4* __restrict__ out, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+    out[i] = float4{0.f, 0.f, 0.f, 0.f};
+}
+
+static int launch_reduce(const float* part, int splits, int64_t n, float* out, int accumulate, hipStream_t st) {
+  const int64_t n4 = n / 4;
+  int64_t blocks = cdiv(n4, 256);
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)blocks), dim3(256), 0, st, (const float4*)part, splits, n4,
+                     (float4*)out, accumulate);
+  return launch_status();
+}
+
+static int launch_zero(float* out, int64_t n, hipStream_t st) {
+  const int64_t n4 = n / 4;
+  int64_t blocks = cdiv(n4, 256);
+  if (blocks > 4096) blocks = 4096;
+  if (blocks == 0) return FP8MLP_OK;
+  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, st, (float4*)out, n4);
+  return launch_status();
+}
+
+// One weight gradient C [Mo, No] = A^T B with A [K, Mo], B [K, No] (K = tokens).
+static int weight_grad(const uint16_t* A, int64_t Mo, const uint16_t* B, int64_t No, int64_t K, float* out,
+                       int accumulate, const BwdPlan& plan, float* part, hipStream_t st) {
+  GemmArgs a{A, Mo, B, No, Mo, No, K, (int)cdiv(Mo, CfgDw::BM), (int)cdiv(No, CfgDw::BN), plan.splits,
+             plan.k_per_split};
+  if (plan.splits == 1) {
+    EpiF32 epi{out, No, 0, accumulate};
+    return launch_gemm<CfgDw>(a, epi, st);
+  }
+  EpiF32 epi{part, No, Mo * No, 0};
+  FP8MLP_TRY(launch_gemm<CfgDw>(a, epi, st));
+  return launch_reduce(part, plan.splits, Mo * No, out, accumulate, st);
+}
+
+}  // namespace fp8mlp
+
+using namespace fp8mlp;
+
+extern "C" {
+
+size_t mlp_relu2_bwd_workspace(int64_t M, int64_t d, int64_t h) {
+  if (M < 0 || d <= 0 || h <= 0) return 0;
+  const BwdPlan p = bwd_plan(M, d, h);
+  return p.dpre_bytes + p.part_bytes;
+}
+
+int mlp_relu2_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* W1, const uint16_t* W2,
+                  const uint16_t* post, uint16_t* dX, float* dW1, float* dW2, int accumulate, int64_t M,
+                  int64_t d, int64_t h, void* workspace, size_t workspace_bytes, void* stream) {
+  FP8MLP_REQUIRE(M >= 0 && d > 0 && h > 0 && d % 64 == 0 && h % 64 == 0, FP8MLP_E_SHAPE);
+  FP8MLP_REQUIRE(accumulate == 0 || accumulate == 1, FP8MLP_E_ARG);
+  FP8MLP_REQUIRE(dW1 && dW2, FP8MLP_E_NULL);
+  if (M > 0) FP8MLP_REQUIRE(dY && X && W1 && W2 && post && dX, FP8MLP_E_NULL);
+  for (const void* p : {(const void*)dY, (const void*)X, (const void*)W1, (const void*)W2, (const void*)post,
+                        (const void*)dX, (const void*)dW1, (const void*)dW2})
+    FP8MLP_REQUIRE(p == nullptr || aligned16(p), FP8MLP_E_ALIGN);
+  const BwdPlan plan = bwd_plan(M, d, h);
+  const size_t need = plan.dpre_bytes + plan.part_bytes;
+  FP8MLP_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), FP8MLP_E_WORKSPACE);
+  FP8MLP_REQUIRE(need == 0 || aligned16(workspace), FP8MLP_E_ALIGN);
+  FP8MLP_TRY(check_device());
+
+  hipStream_t st = (hipStream_t)stream;
+  if (M == 0) {
+    if (!accumulate) {
+      FP8MLP_TRY(launch_zero(dW1, h * d, st));
+      FP8MLP_TRY(launch_zero(dW2, d * h, st));
+    }
+    return FP8MLP_OK;
+  }
+  uint16_t* dpre = (uint16_t*)workspace;
+  float* part = (float*)((char*)workspace + plan.dpre_bytes);
+
+  // 1. dpost = dY W2 with the sqrt(post) epilogue -> dpre
+  {
+    GemmArgs a{dY, d, W2, h, M, h, d, (int)cdiv(M, CfgDpost::BM), (int)cdiv(h, CfgDpost::BN), 1, d};
+    EpiDpre epi{post, dpre, h};
+    FP8MLP_TRY(launch_gemm<CfgDpost>(a, epi, st));
+  }
+  // 2. dX = dpre W1
+  {
+    GemmArgs a{dpre, h, W1, d, M, d, h, (int)cdiv(M, CfgDx::BM), (int)cdiv(d, CfgDx::BN), 1, h};
+    EpiBf16Out epi{dX, d, 0, nullptr, 0.0f, nullptr, nullptr, nullptr};
+    FP8MLP_TRY(launch_gemm<CfgDx>(a, epi, st));
+  }
+  // 3. dW1 = dpre^T X ; 4. dW2 = dY^T post
+  FP8MLP_TRY(weight_grad(dpre, h, X, d, M, dW1, accumulate, plan, part, st));
+  FP8MLP_TRY(weight_grad(dY, d, post, h, M, dW2, accumulate, plan, part, st));
+  return FP8MLP_OK;
+}
+
+}  // extern "C"

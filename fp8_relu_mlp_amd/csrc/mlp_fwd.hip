@@ -1,0 +1,92 @@
+// mlp_relu2_fwd: fused up-projection + ReLU^2 + e4m3 quantisation + partial
+// amax, the partial-amax reduction, and the FP8 (or, at eval, bf16)
+// down-projection.  All launches go to the caller's stream, back to back.
+#include "launch.h"
+
+namespace fp8mlp {
+
+// X [M,d] . W1[h,d]^T : both operands k-contiguous, 256 x 256 tiles.
+using CfgUp = GemmCfg<2, 256, 256, 2, KC, KC>;
+// post_q [M,h] . W2t_q [h,d] : e4m3, the cache is read with transposing LDS loads.
+using CfgDown8 = GemmCfg<1, 192, 256, 2, KC, MNC>;
+// post [M,h] . W2[d,h]^T : bf16 eval path.
+using CfgDownBf16 = GemmCfg<2, 192, 256, 2, KC, KC>;
+
+struct FwdPlan {
+  int64_t tm, tn;          // up-projection tiles
+  size_t partial_bytes;
+};
+static FwdPlan fwd_plan(int64_t M, int64_t h) {
+  FwdPlan p;
+  p.tm = cdiv(M, CfgUp::BM);
+  p.tn = cdiv(h, CfgUp::BN);
+  p.partial_bytes = align_up((size_t)(p.tm * p.tn) * 4, 256);
+  return p;
+}
+
+}  // namespace fp8mlp
+
+using namespace fp8mlp;
+
+extern "C" {
+
+size_t mlp_relu2_fwd_workspace(int64_t M, int64_t d, int64_t h) {
+  if (M < 0 || d <= 0 || h <= 0) return 0;
+  return fwd_plan(M, h).partial_bytes;
+}
+
+int mlp_relu2_fwd(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t* W2t_q,
+                  const float* w2_inv_scale, const uint16_t* W2, const float* amax_prev, float margin,
+                  uint16_t* post, uint8_t* post_q, float* amax_out, float* scale_out, uint16_t* Y, int64_t M,
+                  int64_t d, int64_t h, void* workspace, size_t workspace_bytes, void* stream) {
+  const bool train = mode == FP8MLP_TRAIN_FP8;
+  FP8MLP_REQUIRE(mode == FP8MLP_TRAIN_FP8 || mode == FP8MLP_EVAL_BF16, FP8MLP_E_ARG);
+  FP8MLP_REQUIRE(M >= 0 && d > 0 && h > 0 && d % 64 == 0 && h % 64 == 0, FP8MLP_E_SHAPE);
+  FP8MLP_REQUIRE(!train || h % 128 == 0, FP8MLP_E_SHAPE);
+  FP8MLP_REQUIRE(amax_out != nullptr, FP8MLP_E_NULL);
+  if (M > 0) FP8MLP_REQUIRE(X && W1 && post && Y, FP8MLP_E_NULL);
+  if (train) {
+    FP8MLP_REQUIRE(amax_prev != nullptr, FP8MLP_E_NULL);
+    if (M > 0) FP8MLP_REQUIRE(W2t_q && w2_inv_scale && post_q, FP8MLP_E_NULL);
+    FP8MLP_REQUIRE(margin > 0.0f && margin <= 3.4e38f, FP8MLP_E_ARG);
+  } else if (M > 0) {
+    FP8MLP_REQUIRE(W2 != nullptr, FP8MLP_E_NULL);
+  }
+  for (const void* p : {(const void*)X, (const void*)W1, (const void*)W2t_q, (const void*)W2, (const void*)post,
+                        (const void*)post_q, (const void*)Y})
+    FP8MLP_REQUIRE(p == nullptr || aligned16(p), FP8MLP_E_ALIGN);
+  for (const void* p : {(const void*)w2_inv_scale, (const void*)amax_prev, (const void*)amax_out,
+                        (const void*)scale_out})
+    FP8MLP_REQUIRE(((uintptr_t)p & 3) == 0, FP8MLP_E_ALIGN);
+  const FwdPlan plan = fwd_plan(M, h);
+  FP8MLP_REQUIRE(workspace_bytes >= plan.partial_bytes && (plan.partial_bytes == 0 || workspace),
+                 FP8MLP_E_WORKSPACE);
+  FP8MLP_REQUIRE(plan.partial_bytes == 0 || aligned16(workspace), FP8MLP_E_ALIGN);
+  FP8MLP_TRY(check_device());
+
+  hipStream_t st = (hipStream_t)stream;
+  float* partial = (float*)workspace;
+
+  // 1. up-projection with the fused ReLU^2 / quantise / partial-amax epilogue
+  {
+    GemmArgs a{X, d, W1, d, M, h, d, (int)plan.tm, (int)plan.tn, 1, d};
+    EpiRelu2Quant epi{post, train ? post_q : nullptr, partial, amax_prev, margin, h, (int)plan.tn};
+    FP8MLP_TRY(launch_gemm<CfgUp>(a, epi, st));
+  }
+  // 2. reduce the partial amax tensor; record the scale that was used
+  FP8MLP_TRY(launch_max_small(partial, plan.tm * plan.tn, amax_out, amax_prev, margin, train ? scale_out : nullptr,
+                              st));
+  // 3. down-projection
+  if (train) {
+    GemmArgs a{post_q, h, W2t_q, d, M, d, h, (int)cdiv(M, CfgDown8::BM), (int)cdiv(d, CfgDown8::BN), 1, h};
+    EpiBf16Out epi{Y, d, 1, amax_prev, margin, nullptr, w2_inv_scale, nullptr};
+    FP8MLP_TRY(launch_gemm<CfgDown8>(a, epi, st));
+  } else {
+    GemmArgs a{post, h, W2, h, M, d, h, (int)cdiv(M, CfgDownBf16::BM), (int)cdiv(d, CfgDownBf16::BN), 1, h};
+    EpiBf16Out epi{Y, d, 0, nullptr, 0.0f, nullptr, nullptr, nullptr};
+    FP8MLP_TRY(launch_gemm<CfgDownBf16>(a, epi, st));
+  }
+  return FP8MLP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,194 @@
+/* fp8mlp.h -- C ABI of libfp8mlp, the fused FP8 ReLU^2 MLP path for AMD
+ * Instinct MI355X (gfx950 / CDNA4).
+ *
+ * What it computes (page titles and sections of the speedrun write-ups):
+ *  - "A Retrospective on Our World Records" (Paradigma), Modded-NanoGPT Main
+ *    Track: the MLP down-projection runs in FP8; the fused up-projection
+ *    epilogue writes the BF16 post-activation for backward, an FP8 copy and a
+ *    tiny partial-amax tensor, so the activation is never reread; the FP8
+ *    scale at step t comes from amax(t-1) times a safety margin (delayed
+ *    scaling); a transposed FP8 cache of W2 is refreshed after each optimizer
+ *    update (an exact, non-delayed refresh is viable per its implementation
+ *    notes); the BF16 backward is unchanged.
+ *  - "NanoGPT Speedrun (Track 1)" (Recursive), "Changes vs Record #83": item 1,
+ *    QKV / output projections in float8_e4m3 on the forward pass with weights
+ *    stored transposed; item 4, the ReLU^2 MLP stores only post = relu(pre)^2
+ *    and the backward rebuilds relu(pre) = sqrt(post).
+ *
+ * Conventions for every entry point:
+ *  - Tensors are caller-owned DEVICE memory, row-major and contiguous.
+ *    bf16 tensors are passed as uint16_t bit patterns, e4m3 tensors as uint8_t
+ *    codes of the OCP E4M3FN format (largest finite 448, no infinities).
+ *    Weights use the [out, in] layout: W1 [h, d], W2 [d, h].
+ *  - Every tensor pointer must be 16-byte aligned.  Feature sizes must be
+ *    positive multiples of 64 (the contraction sizes of the e4m3 GEMMs,
+ *    multiples of 128); the token count M may be any value >= 0 (ragged
+ *    tails are masked, M = 0 is a valid empty call).
+ *  - Scalars that change from step to step (amax, scales) live in device
+ *    memory as fp32 so a training step never synchronises with the host.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and runs asynchronously.  The library never synchronises, never
+ *    allocates or frees memory, and keeps no pointer after the call returns;
+ *    buffers must stay alive until the stream has passed the enqueued work.
+ *  - Every call returns FP8MLP_OK (0) or a negative status.  Arguments are
+ *    validated on the host before anything is enqueued, so a call that
+ *    returns an error has launched nothing (FP8MLP_E_HIP, a failed launch, is
+ *    the exception: earlier kernels of the same call may have been enqueued).
+ *  - Calls are stateless and may be issued from several threads; calls that
+ *    share output or workspace buffers must be ordered by the caller.
+ */
+#ifndef FP8MLP_H
+#define FP8MLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8MLP_ABI_VERSION 1
+
+enum {
+  FP8MLP_OK = 0,
+  FP8MLP_E_NULL = -1,      /* a required pointer is NULL */
+  FP8MLP_E_SHAPE = -2,     /* a size is negative, zero where not allowed, or not a multiple of 64 */
+  FP8MLP_E_ALIGN = -3,     /* a tensor pointer is not 16-byte aligned */
+  FP8MLP_E_WORKSPACE = -4, /* workspace missing or smaller than the *_workspace() size */
+  FP8MLP_E_ARCH = -5,      /* the current device is not gfx950 */
+  FP8MLP_E_HIP = -6,       /* a HIP call failed; see fp8mlp_last_hip_error() */
+  FP8MLP_E_ARG = -7        /* any other invalid argument (mode, dtype, margin) */
+};
+enum { FP8MLP_TRAIN_FP8 = 0, FP8MLP_EVAL_BF16 = 1 }; /* mlp_relu2_fwd mode */
+enum { FP8MLP_F32 = 0, FP8MLP_BF16 = 1 };            /* amax_reduce dtype */
+
+int fp8mlp_abi_version(void);
+const char* fp8mlp_status_str(int status);
+/* hipError_t value behind the last FP8MLP_E_HIP returned on this thread. */
+int fp8mlp_last_hip_error(void);
+
+/* ------------------------------------------------------------------------
+ * mlp_relu2_fwd -- one forward of the MLP block.
+ *
+ * TRAIN (mode FP8MLP_TRAIN_FP8), per "A Retrospective on Our World Records",
+ * Main Track:
+ *   pre    = X W1^T                      (bf16 MFMA, fp32 accumulate; never stored)
+ *   post   = bf16(relu(pre)^2)           -> post [M, h]
+ *   scale  = fp32(448 / fp32(margin * amax_prev))   (1 if that is not a
+ *            positive finite number)     -> scale_out (if not NULL)
+ *   post_q = e4m3(fp32(post * scale))    -> post_q [M, h]; round to nearest
+ *            even, saturate to +-448
+ *   partial[tile] = max(post over the tile), then amax_out = max(partial)
+ *   Y      = bf16((post_q . W2t_q) * fp32(1/scale) * w2_inv_scale)   [M, d]
+ *   The scale depends only on amax_prev (the previous step's amax_out), so
+ *   quantisation happens inside the up-projection epilogue and the forward
+ *   never waits for the current amax.
+ * EVAL (mode FP8MLP_EVAL_BF16), per "NanoGPT Speedrun (Track 1)", "Approach"
+ *   item 5 (bf16 at eval): post as above, Y = bf16(post W2^T) with the bf16 W2;
+ *   post_q, W2t_q, w2_inv_scale and amax_prev are not read (may be NULL);
+ *   amax_out is still produced.
+ *
+ * Arguments:
+ *   X [M, d] bf16, W1 [h, d] bf16; d a multiple of 64, h a multiple of 64
+ *   (EVAL) or 128 (TRAIN).
+ *   W2t_q [h, d] e4m3: the transposed W2 cache (fp8_cast_transpose_w2);
+ *   w2_inv_scale: device fp32, its dequantisation multiplier.
+ *   W2 [d, h] bf16: read in EVAL mode only (may be NULL in TRAIN).
+ *   amax_prev: device fp32, amax_out of the previous step.  margin: the
+ *   safety margin (> 0, finite; 2 in the speedrun workload).
+ *   amax_out: device fp32, required.  scale_out: device fp32 or NULL.
+ *   workspace: device memory of mlp_relu2_fwd_workspace(M, d, h) bytes.
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_ARCH, E_ARG, E_HIP.
+ * ---------------------------------------------------------------------- */
+size_t mlp_relu2_fwd_workspace(int64_t M, int64_t d, int64_t h);
+int mlp_relu2_fwd(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t* W2t_q,
+                  const float* w2_inv_scale, const uint16_t* W2, const float* amax_prev, float margin,
+                  uint16_t* post, uint8_t* post_q, float* amax_out, float* scale_out, uint16_t* Y,
+                  int64_t M, int64_t d, int64_t h, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * mlp_relu2_bwd -- the bf16 backward of the block, straight through the FP8
+ * forward ("A Retrospective on Our World Records", Main Track: the BF16
+ * backward path is left unchanged; "NanoGPT Speedrun (Track 1)", "Changes vs
+ * Record #83" item 4: relu(pre) is rebuilt in-kernel as sqrt(post)).
+ *   dpost = dY W2                         (never stored)
+ *   dpre  = bf16(2 * sqrt(post) * dpost)  (kept in the workspace)
+ *   dX    = bf16(dpre W1)                 -> dX [M, d] bf16
+ *   dW1   = dpre^T X                      -> dW1 [h, d] fp32
+ *   dW2   = dY^T post                     -> dW2 [d, h] fp32
+ * accumulate = 0 overwrites dW1 / dW2, 1 adds into them.  The weight
+ * gradients are summed over M in a fixed order (split-k partials reduced in
+ * split order), so repeated calls give identical bits.
+ * Arguments: dY [M, d] bf16, X [M, d] bf16, W1 [h, d] bf16, W2 [d, h] bf16,
+ * post [M, h] bf16 (from mlp_relu2_fwd); workspace of
+ * mlp_relu2_bwd_workspace(M, d, h) bytes.
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_ARCH, E_ARG, E_HIP.
+ * ---------------------------------------------------------------------- */
+size_t mlp_relu2_bwd_workspace(int64_t M, int64_t d, int64_t h);
+int mlp_relu2_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* W1, const uint16_t* W2,
+                  const uint16_t* post, uint16_t* dX, float* dW1, float* dW2, int accumulate, int64_t M,
+                  int64_t d, int64_t h, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_cast_transpose -- bf16 weight W [N, K] -> e4m3 Wt_q [K, N] (the
+ * transposed FP8 weight cache of "A Retrospective on Our World Records",
+ * Main Track, and of "NanoGPT Speedrun (Track 1)", "Changes vs Record #83"
+ * item 1) with one per-tensor scale:
+ *   amax  = max |W|                        -> amax_out (if not NULL)
+ *   scale = *scale_in if scale_in is not NULL, else fp32(448 / amax)
+ *           (the exact, non-delayed refresh; 1 if amax is 0 or not finite)
+ *   Wt_q[k, n] = e4m3(fp32(W[n, k] * scale))   RNE, saturating, sign kept
+ *   scale -> scale_out, fp32(1 / scale) -> inv_scale_out (each if not NULL)
+ * N and K: positive multiples of 16.  workspace: fp8_cast_transpose_workspace
+ * (N, K) bytes (used for the amax reduction).
+ * fp8_cast_transpose_w2 is the same call on W2 [d, h] -> W2t_q [h, d] with the
+ * exact scale, to be run after every update of W2.
+ * ---------------------------------------------------------------------- */
+size_t fp8_cast_transpose_workspace(int64_t N, int64_t K);
+int fp8_cast_transpose(const uint16_t* W, int64_t N, int64_t K, uint8_t* Wt_q, const float* scale_in,
+                       float* scale_out, float* inv_scale_out, float* amax_out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+int fp8_cast_transpose_w2(const uint16_t* W2, int64_t d, int64_t h, uint8_t* W2t_q, float* scale_out,
+                          float* inv_scale_out, float* amax_out, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------------------
+ * amax_reduce -- amax_out = max |x[i]| over n elements of fp32 (dtype
+ * FP8MLP_F32) or bf16 (FP8MLP_BF16) data; 0 for n = 0; NaN if any element is
+ * NaN.  The per-tensor amax that sets an FP8 scale ("A Retrospective on Our
+ * World Records", Main Track: the partial-amax values are reduced later).
+ * The maximum is taken on the bit patterns of |x|, so it is exact and
+ * independent of the reduction order.  workspace: amax_reduce_workspace(n).
+ * ---------------------------------------------------------------------- */
+size_t amax_reduce_workspace(int64_t n);
+int amax_reduce(int dtype, const void* x, int64_t n, float* amax_out, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_scale_from_amax -- device-side scale for an FP8 tensor:
+ *   scale = fp32(448 / fp32(margin * *amax)), 1 if that is not a positive
+ *   finite number; inv_scale = fp32(1 / scale).
+ * margin 1 gives the exact per-tensor scale, margin > 1 with the previous
+ * step's amax the delayed scale ("A Retrospective on Our World Records",
+ * Main Track).  scale_out / inv_scale_out: device fp32 (either may be NULL).
+ * ---------------------------------------------------------------------- */
+int fp8_scale_from_amax(const float* amax, float margin, float* scale_out, float* inv_scale_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_linear -- forward of an FP8 projection ("NanoGPT Speedrun (Track 1)",
+ * "Changes vs Record #83" item 1: QKV and output projections in e4m3 on the
+ * forward pass, weights stored transposed):
+ *   Xq = e4m3(fp32(X * *x_scale))        (quantised inside the GEMM, never stored)
+ *   Y  = bf16((Xq . Wt_q) * fp32(1 / *x_scale) * *w_inv_scale)
+ * X [M, K] bf16, Wt_q [K, N] e4m3 (from fp8_cast_transpose), Y [M, N] bf16.
+ * x_scale, w_inv_scale: device fp32.  x_amax_out: device fp32 or NULL; if
+ * given it receives max |X| (for the next step's delayed scale).
+ * K: a positive multiple of 128, N: a positive multiple of 64; M >= 0.
+ * ---------------------------------------------------------------------- */
+int fp8_linear(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, const float* w_inv_scale,
+               uint16_t* Y, float* x_amax_out, int64_t M, int64_t K, int64_t N, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8MLP_H */

@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+* libfp8mlp.so loads and exports every function include/fp8mlp.h declares;
+* the Python binding declares exactly those functions;
+* workspace queries and argument validation (which runs on the host before
+  any device call) return the documented status codes.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8mlp.h")
+LIBP = os.path.join(ROOT, "fp8_relu_mlp_amd", "libfp8mlp.so")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_WS, E_ARCH, E_HIP, E_ARG = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIBP):
+        pytest.fail("libfp8mlp.so is not built (run __graft_entry__.build())")
+    from fp8_relu_mlp_amd import _lib
+    return _lib.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared()
+    for must in ("mlp_relu2_fwd", "mlp_relu2_bwd", "fp8_cast_transpose_w2", "amax_reduce", "fp8_linear"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    raw = ctypes.CDLL(LIBP)
+    missing = [n for n in declared() if not hasattr(raw, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_the_header(L):
+    from fp8_relu_mlp_amd import _lib
+    assert sorted(_lib.SIGNATURES) == declared()
+
+
+def test_version_and_status_strings(L):
+    assert L.fp8mlp_abi_version() == 1
+    for st in (OK, E_NULL, E_SHAPE, E_ALIGN, E_WS, E_ARCH, E_HIP, E_ARG):
+        assert len(L.fp8mlp_status_str(st)) >= 2
+    assert L.fp8mlp_status_str(12345) == b"unknown status"
+
+
+def test_workspace_sizes(L):
+    M, d, h = 49152, 768, 3072
+    assert L.mlp_relu2_fwd_workspace(M, d, h) == 192 * 12 * 4 + (256 - (192 * 12 * 4) % 256) % 256
+    bw = L.mlp_relu2_bwd_workspace(M, d, h)
+    assert bw >= M * h * 2                      # dpre
+    assert L.mlp_relu2_fwd_workspace(0, d, h) == 0
+    assert L.amax_reduce_workspace(100) == 0
+    assert L.amax_reduce_workspace(1 << 20) > 0
+    assert L.fp8_cast_transpose_workspace(768, 3072) >= 256
+
+
+def _fwd(L, **kw):
+    args = dict(mode=0, X=16, W1=16, W2t_q=16, w2_inv=16, W2=None, amax_prev=16, margin=2.0, post=16,
+                post_q=16, amax_out=16, scale_out=None, Y=16, M=256, d=128, h=512, ws=16, wsb=1 << 20,
+                stream=None)
+    args.update(kw)
+    return L.mlp_relu2_fwd(*args.values())
+
+
+def test_fwd_validation_before_any_device_call(L):
+    assert _fwd(L, mode=7) == E_ARG
+    assert _fwd(L, d=100) == E_SHAPE
+    assert _fwd(L, h=192) == E_SHAPE            # train needs h % 128 == 0
+    assert _fwd(L, M=-1) == E_SHAPE
+    assert _fwd(L, X=None) == E_NULL
+    assert _fwd(L, amax_out=None) == E_NULL
+    assert _fwd(L, post_q=None) == E_NULL
+    assert _fwd(L, X=24) == E_ALIGN
+    assert _fwd(L, margin=0.0) == E_ARG
+    assert _fwd(L, margin=float("nan")) == E_ARG
+    assert _fwd(L, ws=None) == E_WS
+    assert _fwd(L, wsb=8) == E_WS
+    assert _fwd(L, mode=1, W2=None) == E_NULL   # eval needs the bf16 W2
+
+
+def test_bwd_and_misc_validation(L):
+    b = lambda **kw: L.mlp_relu2_bwd(*dict(dict(dY=16, X=16, W1=16, W2=16, post=16, dX=16, dW1=16, dW2=16,
+                                                 acc=0, M=256, d=128, h=512, ws=16, wsb=1 << 30,
+                                                 stream=None), **kw).values())
+    assert b(acc=2) == E_ARG
+    assert b(h=100) == E_SHAPE
+    assert b(dW1=None) == E_NULL
+    assert b(post=40) == E_ALIGN
+    assert b(wsb=10) == E_WS
+    assert L.amax_reduce(5, 16, 10, 16, None, 0, None) == E_ARG
+    assert L.amax_reduce(0, 16, -1, 16, None, 0, None) == E_SHAPE
+    assert L.amax_reduce(0, 16, 10, None, None, 0, None) == E_NULL
+    assert L.amax_reduce(0, 16, 1 << 20, 16, None, 0, None) == E_WS
+    assert L.fp8_cast_transpose(16, 30, 64, 16, None, None, None, None, 16, 1 << 20, None) == E_SHAPE
+    assert L.fp8_cast_transpose(None, 64, 64, 16, None, None, None, None, 16, 1 << 20, None) == E_NULL
+    assert L.fp8_cast_transpose(16, 64, 64, 16, None, None, None, None, None, 0, None) == E_WS
+    assert L.fp8_scale_from_amax(None, 2.0, None, None, None) == E_NULL
+    assert L.fp8_scale_from_amax(16, -1.0, None, None, None) == E_ARG
+    assert L.fp8_linear(16, 16, 16, 16, 16, None, 100, 192, 256, None) == E_SHAPE   # K % 128
+    assert L.fp8_linear(16, None, 16, 16, 16, None, 100, 256, 256, None) == E_NULL
+    assert L.fp8_linear(16, 16, 16, 16, 17, None, 100, 256, 256, None) == E_ALIGN
