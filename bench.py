@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused FP8 ReLU^2 MLP block on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one training pass of the MLP block over one batch of synthetic
+GPT-2-small-shaped tokens (M=49152, d=768, h=3072, margin 2):
+  mlp_relu2_fwd (TRAIN: up-projection + ReLU^2 + e4m3 quantisation with the
+  delayed scale + partial amax, amax reduction, e4m3 down-projection),
+  mlp_relu2_bwd (dgrad with sqrt(post), dX, dW1, dW2),
+  fp8_cast_transpose_w2 (the W2 cache refresh that follows each update),
+with the measured amax carried to the next step as its amax_prev.
+Inputs are resident in HBM before timing starts; W warm-up steps are not
+timed; K steps are timed with HIP events between two device synchronisations.
+
+value = 12*M*d*h / t_step in TFLOP/s (the six GEMMs of forward + backward).
+One JSON line goes to stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+M, D, H = 49152, 768, 3072
+MARGIN = 2.0
+PEAK_BF16 = 2500.0    # TFLOP/s, MI355X dense bf16 MFMA (published)
+PEAK_FP8 = 5000.0     # TFLOP/s, MI355X dense fp8 MFMA (published)
+PEAK_HBM = 8000.0     # GB/s
+METRIC = "MLP fwd+bwd TFLOP/s and % of MFMA peak, M=49152 d=768 h=3072, 1 GPU"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# algorithmic work per launch of each kernel at (M, d, h): (flops, bytes, dtype peak)
+def kernel_work(M, d, h):
+    b16, b8, f32 = 2, 1, 4
+    mdh2 = 2.0 * M * d * h
+    return {
+        "up_gemm_relu2_quant": (mdh2, M * d * b16 + h * d * b16 + M * h * (b16 + b8), PEAK_BF16),
+        "down_gemm_e4m3": (mdh2, M * h * b8 + h * d * b8 + M * d * b16, PEAK_FP8),
+        "dpost_gemm_dpre": (mdh2, M * d * b16 + d * h * b16 + 2 * M * h * b16, PEAK_BF16),
+        "dx_gemm": (mdh2, M * h * b16 + h * d * b16 + M * d * b16, PEAK_BF16),
+        "dw1_gemm": (mdh2, M * h * b16 + M * d * b16 + h * d * f32, PEAK_BF16),
+        "dw2_gemm": (mdh2, M * d * b16 + M * h * b16 + d * h * f32, PEAK_BF16),
+        "down_gemm_bf16_eval": (mdh2, M * h * b16 + h * d * b16 + M * d * b16, PEAK_BF16),
+    }
+
+
+def mixed_floor_us(M, d, h):
+    mdh = float(M) * d * h
+    return (10 * mdh / (PEAK_BF16 * 1e12) + 2 * mdh / (PEAK_FP8 * 1e12)) * 1e6
+
+
+def cpu_baseline(ins, amax_prev, target_s=15.0):
+    """The oracle (as it stands) on a bounded sample of the same workload:
+    the first Ms token rows, fwd (TRAIN) + bwd + the W2 cache refresh."""
+    import numpy as np
+    from oracle import formats as F
+    from oracle import mlp as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+
+    def run(ms):
+        t0 = time.perf_counter()
+        W2t, _, inv_sw, _ = O.cast_transpose(ins["W2"])
+        out = O.mlp_fwd(ins["X"][:ms], ins["W1"], W2t, inv_sw, amax_prev, MARGIN)
+        O.mlp_bwd(ins["dY"][:ms], ins["X"][:ms], ins["W1"], ins["W2"], F.bf16_to_f64(out["post"]))
+        return time.perf_counter() - t0
+
+    t1 = run(512)
+    ms = int(min(16384, max(512, 512 * target_s / max(t1, 1e-3))) // 512 * 512)
+    t = run(ms)
+    return {"value": 12.0 * ms * D * H / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {ms} of {M} token rows (d={D}, h={H}), fwd+bwd+W2 refresh, {t:.1f} s",
+            "seconds": round(t, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the FP8-linear / eval / ablation lines")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); multi-GPU runs are not part of "
+              "this build: the data-parallel sharding is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_relu_mlp_amd as fm
+    from fp8_relu_mlp_amd import synth
+
+    dev = torch.device("cuda:0")
+    fm.lib()
+    log("generating inputs")
+    ins = synth.mlp_inputs(M, D, H, synth.WORKLOADS["fwdbwd"][3], with_dy=True)
+
+    def bf(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X, W1, W2, dY = bf(ins["X"]), bf(ins["W1"]), bf(ins["W2"]), bf(ins["dY"])
+    blk = fm.Relu2MLP(W1, W2, margin=MARGIN, amax_init=1.0)
+    post = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    post_q = torch.empty((M, H), dtype=torch.uint8, device=dev)
+    Y = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+    dW1 = torch.empty((H, D), dtype=torch.float32, device=dev)
+    dW2 = torch.empty((D, H), dtype=torch.float32, device=dev)
+    L = fm.lib()
+    ws_f = torch.empty(max(1, L.mlp_relu2_fwd_workspace(M, D, H)), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(1, L.mlp_relu2_bwd_workspace(M, D, H)), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(max(1, L.fp8_cast_transpose_workspace(D, H)), dtype=torch.uint8, device=dev)
+
+    def step():
+        blk.forward(X, post=post, post_q=post_q, Y=Y, workspace=ws_f)
+        blk.backward(dY, X, post, dX, dW1, dW2, workspace=ws_b)
+        blk.refresh_w2_cache(workspace=ws_c)
+
+    blk.forward(X, post=post, post_q=post_q, Y=Y, workspace=ws_f)   # bootstrap amax_prev
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = 12.0 * M * D * H
+    value = flops / (ms * 1e-3) / 1e12
+    floor_us = mixed_floor_us(M, D, H)
+    log(f"{ms:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    # per-kernel durations: the same steps again with every launch bracketed by events
+    log("per-kernel timing pass")
+    with fm.KernelTimer(64 * args.steps) as kt:
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    per = {}
+    for name, t in kt.records():
+        per.setdefault(name, []).append(t)
+    work = kernel_work(M, D, H)
+    kernels = {}
+    for name, ts in per.items():
+        avg_us = 1e3 * sum(ts) / len(ts)
+        entry = {"launches_per_step": len(ts) / args.steps, "avg_us": round(avg_us, 2)}
+        if name in work:
+            fl, by, peak = work[name]
+            entry.update(tflops=round(fl / (avg_us * 1e-6) / 1e12, 1), frac_mfma=round(fl / (avg_us * 1e-6) / 1e12 / peak, 4),
+                         hbm_gbs_alg=round(by / (avg_us * 1e-6) / 1e9, 1))
+        kernels[name] = entry
+    gemms = [n for n in kernels if n in work]
+    dom = max(gemms, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches_per_step"])
+    fl, by, peak = work[dom]
+    achieved = fl / (kernels[dom]["avg_us"] * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "algorithmic_flops_per_launch": fl, "algorithmic_bytes_per_launch": by}
+
+    extras = {}
+    if not args.no_extras:
+        log("extra measurements")
+        extras = extra_measurements(fm, torch, dev, X, W2, blk, post, post_q, Y, ws_f)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on a bounded sample)")
+        cpu = cpu_baseline(ins, float(blk.amax_prev.item()))
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16+e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": "relu2_mlp_fwd_bwd_gpt2_small", "M": M, "d": D, "h": H, "margin": MARGIN,
+                   "step": "fwd(train)+bwd+W2 cache refresh"},
+        "pct_mixed_mfma_peak": round(100.0 * floor_us / (ms * 1e3), 2),
+        "mixed_mfma_floor_us": round(floor_us, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "extras": extras,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def extra_measurements(fm, torch, dev, X, W2, blk, post, post_q, Y, ws_f, reps=20):
+    """Side measurements (not part of `value`): forward-only TRAIN vs EVAL
+    (bf16 down-projection ablation), the FP8 attention projections and the
+    W2 cache refresh."""
+    import numpy as np
+    from fp8_relu_mlp_amd import synth
+
+    def timed(fn, reps=reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    out = {}
+    mdh2 = 2.0 * M * D * H
+    t_tr = timed(lambda: blk.forward(X, post=post, post_q=post_q, Y=Y, carry=False, workspace=ws_f))
+    t_ev = timed(lambda: blk.forward(X, mode=fm.EVAL_BF16, post=post, Y=Y, carry=False, workspace=ws_f))
+    out["fwd_train_fp8_ms"] = round(t_tr, 4)
+    out["fwd_eval_bf16_ms"] = round(t_ev, 4)
+    out["fwd_train_tflops"] = round(2 * mdh2 / (t_tr * 1e-3) / 1e12, 1)
+    ws_c = torch.empty(max(1, fm.lib().fp8_cast_transpose_workspace(D, H)), dtype=torch.uint8, device=dev)
+    t_w2 = timed(lambda: fm.fp8_cast_transpose_w2(W2, blk.W2t_q, blk.w2_scale, blk.w2_inv_scale, blk.w2_amax,
+                                                  workspace=ws_c))
+    out["w2_refresh_us"] = round(t_w2 * 1e3, 2)
+    out["w2_refresh_gbs_alg"] = round((D * H * 2 * 2 + D * H) / (t_w2 * 1e-3) / 1e9, 1)
+
+    # FP8 attention projections: QKV [49152,768]x[768,2304], O [49152,768]x[768,768]
+    a = synth.attn_inputs()
+
+    def bf(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    for tag, xk, wk, n in (("qkv", "X", "Wqkv", 2304), ("o", "Xo", "Wo", 768)):
+        Xa, Wa = bf(a[xk]), bf(a[wk])
+        Wt = torch.empty((D, n), dtype=torch.uint8, device=dev)
+        inv_w = torch.zeros(1, dtype=torch.float32, device=dev)
+        fm.fp8_cast_transpose(Wa, Wt, inv_scale_out=inv_w)
+        amax = torch.zeros(1, dtype=torch.float32, device=dev)
+        fm.amax_reduce(Xa, amax)
+        sx = torch.zeros(1, dtype=torch.float32, device=dev)
+        fm.fp8_scale_from_amax(amax, 1.0, sx)
+        Ya = torch.empty((Xa.shape[0], n), dtype=torch.bfloat16, device=dev)
+        wsl = torch.empty(max(1, fm.lib().fp8_linear_workspace(Xa.shape[0], D)), dtype=torch.uint8, device=dev)
+        t = timed(lambda: fm.fp8_linear(Xa, sx, Wt, inv_w, Ya, workspace=wsl))
+        fl = 2.0 * Xa.shape[0] * D * n
+        by = Xa.shape[0] * D * 2 + D * n + Xa.shape[0] * n * 2
+        out[f"fp8_linear_{tag}_us"] = round(t * 1e3, 2)
+        out[f"fp8_linear_{tag}_tflops"] = round(fl / (t * 1e-3) / 1e12, 1)
+        out[f"fp8_linear_{tag}_frac_fp8_peak"] = round(fl / (t * 1e-3) / 1e12 / PEAK_FP8, 4)
+        out[f"fp8_linear_{tag}_hbm_gbs_alg"] = round(by / (t * 1e-3) / 1e9, 1)
+    return out
+
+
+if __name__ == "__main__":
+    main()

@@ -22,7 +22,7 @@ F32 = 0
 BF16 = 1
 
 __all__ = ["mlp_relu2_fwd", "mlp_relu2_bwd", "fp8_cast_transpose", "fp8_cast_transpose_w2", "amax_reduce",
-           "fp8_scale_from_amax", "fp8_linear", "Relu2MLP", "Fp8MlpError", "TRAIN_FP8", "EVAL_BF16"]
+           "fp8_scale_from_amax", "fp8_linear", "Relu2MLP", "KernelTimer", "Fp8MlpError", "TRAIN_FP8", "EVAL_BF16"]
 
 
 def _p(t):
@@ -116,12 +116,51 @@ def fp8_scale_from_amax(amax, margin, scale_out=None, inv_scale_out=None, stream
         _p(amax), float(margin), _p(scale_out), _p(inv_scale_out), _stream(stream)))
 
 
-def fp8_linear(X, x_scale, Wt_q, w_inv_scale, Y, x_amax_out=None, stream=None):
+def fp8_linear(X, x_scale, Wt_q, w_inv_scale, Y, x_amax_out=None, workspace=None, stream=None):
     """Y [M,N] = FP8 linear of X [M,K] bf16 with Wt_q [K,N] e4m3."""
     M, K = X.shape
     N = Wt_q.shape[1]
-    check("fp8_linear", lib().fp8_linear(
-        _p(X), _p(x_scale), _p(Wt_q), _p(w_inv_scale), _p(Y), _p(x_amax_out), M, K, N, _stream(stream)))
+    L = lib()
+    ws, wsb = _ws(L.fp8_linear_workspace(M, K), workspace, X.device)
+    check("fp8_linear", L.fp8_linear(
+        _p(X), _p(x_scale), _p(Wt_q), _p(w_inv_scale), _p(Y), _p(x_amax_out), M, K, N, _p(ws), wsb,
+        _stream(stream)))
+
+
+class KernelTimer:
+    """Context manager around the library's per-kernel timing events.
+
+        with KernelTimer(4096) as kt:
+            ...library calls...
+        torch.cuda.synchronize()
+        kt.records()   # [(kernel name, milliseconds), ...] in launch order
+    """
+
+    def __init__(self, capacity=4096):
+        self.capacity = capacity
+        self.n = 0
+
+    def __enter__(self):
+        check("fp8mlp_timing_start", lib().fp8mlp_timing_start(self.capacity))
+        return self
+
+    def __exit__(self, *exc):
+        self.n = lib().fp8mlp_timing_stop()
+        return False
+
+    def records(self):
+        import ctypes
+        L = lib()
+        out = []
+        for i in range(self.n):
+            name = ctypes.c_char_p()
+            ms = ctypes.c_float()
+            check("fp8mlp_timing_get", L.fp8mlp_timing_get(i, ctypes.byref(name), ctypes.byref(ms)))
+            out.append((name.value.decode(), ms.value))
+        return out
+
+    def dropped(self):
+        return lib().fp8mlp_timing_dropped()
 
 
 class Relu2MLP:
@@ -148,10 +187,11 @@ class Relu2MLP:
             self.amax_prev.fill_(float(amax_init))
         self.refresh_w2_cache()
 
-    def refresh_w2_cache(self, stream=None):
-        fp8_cast_transpose_w2(self.W2, self.W2t_q, self.w2_scale, self.w2_inv_scale, self.w2_amax, stream=stream)
+    def refresh_w2_cache(self, workspace=None, stream=None):
+        fp8_cast_transpose_w2(self.W2, self.W2t_q, self.w2_scale, self.w2_inv_scale, self.w2_amax,
+                              workspace=workspace, stream=stream)
 
-    def forward(self, X, mode=TRAIN_FP8, post=None, post_q=None, Y=None, carry=True, stream=None):
+    def forward(self, X, mode=TRAIN_FP8, post=None, post_q=None, Y=None, carry=True, workspace=None, stream=None):
         """Returns (Y, post, post_q).  With carry, the amax measured here
         becomes amax_prev for the next call."""
         M = X.shape[0]
@@ -162,7 +202,7 @@ class Relu2MLP:
         Y = torch.empty((M, self.d), dtype=torch.bfloat16, device=dev) if Y is None else Y
         mlp_relu2_fwd(mode, X, self.W1, self.W2t_q, self.w2_inv_scale, self.W2, self.amax_prev, self.margin,
                       post, post_q if mode == TRAIN_FP8 else None, self._amax_next,
-                      self.scale_used if mode == TRAIN_FP8 else None, Y, stream=stream)
+                      self.scale_used if mode == TRAIN_FP8 else None, Y, workspace=workspace, stream=stream)
         if carry:
             self.amax_prev, self._amax_next = self._amax_next, self.amax_prev
         return Y, post, post_q
@@ -172,10 +212,10 @@ class Relu2MLP:
         """The amax measured by the most recent carried forward."""
         return self.amax_prev
 
-    def backward(self, dY, X, post, dX=None, dW1=None, dW2=None, accumulate=False, stream=None):
+    def backward(self, dY, X, post, dX=None, dW1=None, dW2=None, accumulate=False, workspace=None, stream=None):
         dev = X.device
         dX = torch.empty_like(X) if dX is None else dX
         dW1 = torch.empty((self.h, self.d), dtype=torch.float32, device=dev) if dW1 is None else dW1
         dW2 = torch.empty((self.d, self.h), dtype=torch.float32, device=dev) if dW2 is None else dW2
-        mlp_relu2_bwd(dY, X, self.W1, self.W2, post, dX, dW1, dW2, accumulate, stream=stream)
+        mlp_relu2_bwd(dY, X, self.W1, self.W2, post, dX, dW1, dW2, accumulate, workspace=workspace, stream=stream)
         return dX, dW1, dW2

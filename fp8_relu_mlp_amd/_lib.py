@@ -34,7 +34,12 @@ SIGNATURES = {
     "amax_reduce_workspace": (c_size, [c_i64]),
     "amax_reduce": (c_int, [c_int, vp, c_i64, vp, vp, c_size, vp]),
     "fp8_scale_from_amax": (c_int, [vp, c_float, vp, vp, vp]),
-    "fp8_linear": (c_int, [vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, vp]),
+    "fp8_linear_workspace": (c_size, [c_i64, c_i64]),
+    "fp8_linear": (c_int, [vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, vp, c_size, vp]),
+    "fp8mlp_timing_start": (c_int, [c_int]),
+    "fp8mlp_timing_stop": (c_int, []),
+    "fp8mlp_timing_get": (c_int, [c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(c_float)]),
+    "fp8mlp_timing_dropped": (c_int, []),
 }
 
 

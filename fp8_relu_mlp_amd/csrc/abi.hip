@@ -120,6 +120,7 @@ size_t amax_ws_bytes(int64_t n) { return n <= kAmaxSmall ? 0 : (size_t)kAmaxBloc
 
 int launch_max_small(const float* x, int64_t n, float* out, const float* amax_prev, float margin,
                      float* scale_out, hipStream_t stream) {
+  TraceScope trace("amax_final", stream);
   hipLaunchKernelGGL(k_max_final, dim3(1), dim3(256), 0, stream, (const uint32_t*)x, n, out, amax_prev, margin,
                      scale_out);
   return launch_status();
@@ -128,6 +129,7 @@ int launch_max_small(const float* x, int64_t n, float* out, const float* amax_pr
 int launch_amax(int dtype, const void* x, int64_t n, float* out, void* workspace, size_t ws_bytes,
                 hipStream_t stream) {
   if (n <= kAmaxSmall) {
+    TraceScope trace("amax_small", stream);
     if (dtype == FP8MLP_F32)
       hipLaunchKernelGGL(k_amax_small<FP8MLP_F32>, dim3(1), dim3(256), 0, stream, x, n, out);
     else
@@ -138,11 +140,15 @@ int launch_amax(int dtype, const void* x, int64_t n, float* out, void* workspace
   int64_t blocks = cdiv(cdiv(n, per), 256 * 4);
   if (blocks > kAmaxBlocks) blocks = kAmaxBlocks;
   uint32_t* partial = (uint32_t*)workspace;
-  if (dtype == FP8MLP_F32)
-    hipLaunchKernelGGL(k_amax_partial<FP8MLP_F32>, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, partial);
-  else
-    hipLaunchKernelGGL(k_amax_partial<FP8MLP_BF16>, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, partial);
+  {
+    TraceScope trace("amax_partial", stream);
+    if (dtype == FP8MLP_F32)
+      hipLaunchKernelGGL(k_amax_partial<FP8MLP_F32>, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, partial);
+    else
+      hipLaunchKernelGGL(k_amax_partial<FP8MLP_BF16>, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, partial);
+  }
   FP8MLP_TRY(launch_status());
+  TraceScope trace("amax_final", stream);
   hipLaunchKernelGGL(k_max_final, dim3(1), dim3(256), 0, stream, (const uint32_t*)partial, blocks, out,
                      (const float*)nullptr, 0.0f, (float*)nullptr);
   return launch_status();
@@ -238,6 +244,7 @@ int fp8_scale_from_amax(const float* amax, float margin, float* scale_out, float
   FP8MLP_REQUIRE(amax != nullptr, FP8MLP_E_NULL);
   FP8MLP_REQUIRE(margin > 0.0f && margin <= 3.4e38f, FP8MLP_E_ARG);
   FP8MLP_TRY(check_device());
+  TraceScope trace("scale_from_amax", (hipStream_t)stream);
   hipLaunchKernelGGL(k_scale_from_amax, dim3(1), dim3(1), 0, (hipStream_t)stream, amax, margin, scale_out,
                      inv_scale_out);
   return launch_status();
@@ -266,6 +273,7 @@ int fp8_cast_transpose(const uint16_t* W, int64_t N, int64_t K, uint8_t* Wt_q, c
     FP8MLP_TRY(launch_amax(FP8MLP_BF16, W, N * K, amax_slot, (char*)workspace + 256, workspace_bytes - 256, st));
   }
   dim3 grid((unsigned)cdiv(K, 64), (unsigned)cdiv(N, 64));
+  TraceScope trace("cast_transpose", st);
   hipLaunchKernelGGL(k_cast_transpose, grid, dim3(256), 0, st, W, N, K, Wt_q, scale_in, (const float*)amax_slot,
                      scale_out, inv_scale_out, amax_out);
   return launch_status();

@@ -91,14 +91,9 @@ struct EpiBf16Out {
   float margin;
   const float* x_scale;
   const float* w_inv;
-  float* qamax_out;       // mode 2: receives max |A| (atomic max on bit patterns), or nullptr
 
   template <class C>
   __device__ __forceinline__ void run(const TileCtx& c, f32x16 (&acc)[C::FM][C::FN], FP8MLP_LDS char*) {
-    if (qamax_out && c.tn == 0) {
-      const uint32_t v = wave_max_u32(c.qamax);
-      if (c.lane == 0) atomicMax((unsigned int*)qamax_out, v);
-    }
     float inv_s = 1.0f, inv_w = 1.0f;
     if (mode == 1) {
       inv_s = 1.0f / scale_from_amax(*amax_prev, margin);

@@ -40,6 +40,18 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
     if (!(cond)) return (status);        \
   } while (0)
 
+// Brackets one kernel launch with timing events while fp8mlp_timing_start is
+// in effect on this thread (trace.hip); a no-op otherwise.
+class TraceScope {
+ public:
+  TraceScope(const char* name, hipStream_t s);
+  ~TraceScope();
+
+ private:
+  hipStream_t stream_;
+  int slot_;
+};
+
 // Shared launchers (defined in abi.hip) used by several entry points.
 // Reduce n fp32 values that are >= +0 or NaN to their maximum, written to
 // out (and, if scale_out is given, the delayed scale from amax_prev/margin).

@@ -1,16 +1,49 @@
-// fp8_linear: FP8 forward projection with the activation quantised inside the
-// GEMM ("NanoGPT Speedrun (Track 1)", "Changes vs Record #83" item 1: QKV and
-// output projections in float8_e4m3 on the forward pass, weights stored
-// transposed).  The bf16 activation tile is loaded into LDS, scaled and
-// encoded to e4m3 there, and fed to the e4m3 MFMA; it never goes back to HBM.
+// fp8_linear: FP8 forward projection ("NanoGPT Speedrun (Track 1)", "Changes
+// vs Record #83" item 1: QKV and output projections in float8_e4m3 on the
+// forward pass, weights stored transposed).
+//
+// Two launches: a bandwidth-bound pass quantises the bf16 activation once
+// (e4m3, RNE, saturating; optionally also max |X|), then the e4m3 MFMA GEMM
+// reads the quantised copy.  Quantising inside the GEMM instead would repeat
+// the conversion in every one of the N / BN column blocks that share an
+// activation tile, and on CDNA4 that conversion is vector-ALU work the
+// matrix cores cannot hide.
 #include "launch.h"
 
 namespace fp8mlp {
 
-// X [M,K] bf16 (quantised on load) . Wt_q [K,N] e4m3 (transposing LDS reads)
-using CfgLin = GemmCfg<1, 128, 256, 2, KC, MNC, true>;
+// Xq [M,K] e4m3 . Wt_q [K,N] e4m3 (transposing LDS reads)
+using CfgLin = GemmCfg<1, 192, 128, 128, 2, 2, KC, MNC, true>;
 
 __global__ void k_zero_scalar(float* p) { *p = 0.0f; }
+
+// Xq = e4m3(fp32(X * s)); 16 elements per thread and step; amax_out, when
+// given, receives max |X| through an atomic max on bit patterns.
+__global__ void __launch_bounds__(256) k_quantize(const uint16_t* __restrict__ X, int64_t n16,
+                                                  const float* __restrict__ scale, uint8_t* __restrict__ Xq,
+                                                  float* amax_out) {
+  const float s = *scale;
+  uint32_t mx = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) {
+    const i32x4 a = __builtin_nontemporal_load((const i32x4*)X + 2 * i);
+    const i32x4 b = __builtin_nontemporal_load((const i32x4*)X + 2 * i + 1);
+    uint32_t w[8] = {(uint32_t)a[0], (uint32_t)a[1], (uint32_t)a[2], (uint32_t)a[3],
+                     (uint32_t)b[0], (uint32_t)b[1], (uint32_t)b[2], (uint32_t)b[3]};
+    i32x4 q;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      mx = max_abs_bf16x2(mx, w[2 * j]);
+      mx = max_abs_bf16x2(mx, w[2 * j + 1]);
+      q[j] = (int)pack_e4m3x4(bf16_lo(w[2 * j]) * s, bf16_hi(w[2 * j]) * s, bf16_lo(w[2 * j + 1]) * s,
+                              bf16_hi(w[2 * j + 1]) * s);
+    }
+    *((i32x4*)Xq + i) = q;
+  }
+  if (amax_out) {
+    mx = wave_max_u32(mx);
+    if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)amax_out, mx);
+  }
+}
 
 }  // namespace fp8mlp
 
@@ -18,8 +51,14 @@ using namespace fp8mlp;
 
 extern "C" {
 
+size_t fp8_linear_workspace(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0) return 0;
+  return align_up((size_t)(M * K), 256);
+}
+
 int fp8_linear(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, const float* w_inv_scale,
-               uint16_t* Y, float* x_amax_out, int64_t M, int64_t K, int64_t N, void* stream) {
+               uint16_t* Y, float* x_amax_out, int64_t M, int64_t K, int64_t N, void* workspace,
+               size_t workspace_bytes, void* stream) {
   FP8MLP_REQUIRE(M >= 0 && K > 0 && N > 0 && K % 128 == 0 && N % 64 == 0, FP8MLP_E_SHAPE);
   FP8MLP_REQUIRE(x_scale && w_inv_scale && Wt_q, FP8MLP_E_NULL);
   if (M > 0) FP8MLP_REQUIRE(X && Y, FP8MLP_E_NULL);
@@ -27,15 +66,29 @@ int fp8_linear(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, con
     FP8MLP_REQUIRE(p == nullptr || aligned16(p), FP8MLP_E_ALIGN);
   for (const void* p : {(const void*)x_scale, (const void*)w_inv_scale, (const void*)x_amax_out})
     FP8MLP_REQUIRE(((uintptr_t)p & 3) == 0, FP8MLP_E_ALIGN);
+  const size_t need = fp8_linear_workspace(M, K);
+  FP8MLP_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), FP8MLP_E_WORKSPACE);
+  FP8MLP_REQUIRE(need == 0 || aligned16(workspace), FP8MLP_E_ALIGN);
   FP8MLP_TRY(check_device());
   hipStream_t st = (hipStream_t)stream;
   if (x_amax_out) {
+    TraceScope trace("zero_scalar", st);
     hipLaunchKernelGGL(k_zero_scalar, dim3(1), dim3(1), 0, st, x_amax_out);
     FP8MLP_TRY(launch_status());
   }
-  GemmArgs a{X, K, Wt_q, N, M, N, K, (int)cdiv(M, CfgLin::BM), (int)cdiv(N, CfgLin::BN), 1, K, x_scale};
-  EpiBf16Out epi{Y, N, 2, nullptr, 0.0f, x_scale, w_inv_scale, x_amax_out};
-  return launch_gemm<CfgLin>(a, epi, st);
+  if (M == 0) return FP8MLP_OK;
+  uint8_t* Xq = (uint8_t*)workspace;
+  {
+    const int64_t n16 = M * K / 16;   // K % 128 == 0
+    int64_t blocks = cdiv(n16, 256 * 4);
+    if (blocks > 4096) blocks = 4096;
+    TraceScope trace("quantize_e4m3", st);
+    hipLaunchKernelGGL(k_quantize, dim3((unsigned)blocks), dim3(256), 0, st, X, n16, x_scale, Xq, x_amax_out);
+    FP8MLP_TRY(launch_status());
+  }
+  GemmArgs a{Xq, K, Wt_q, N, M, N, K, (int)cdiv(M, CfgLin::BM), (int)cdiv(N, CfgLin::BN), 1, K, 0};
+  EpiBf16Out epi{Y, N, 2, nullptr, 0.0f, x_scale, w_inv_scale};
+  return launch_gemm<CfgLin>("fp8_linear_gemm", a, epi, st);
 }
 
 }  // extern "C"

@@ -8,11 +8,11 @@
 namespace fp8mlp {
 
 // dY [M,d] . W2 [d,h]: W2 is k-major here, read with transposing LDS loads.
-using CfgDpost = GemmCfg<2, 256, 256, 2, KC, MNC>;
+using CfgDpost = GemmCfg<2, 256, 128, 64, 2, 2, KC, MNC, true>;
 // dpre [M,h] . W1 [h,d]
-using CfgDx = GemmCfg<2, 192, 256, 2, KC, MNC>;
+using CfgDx = GemmCfg<2, 192, 128, 64, 2, 2, KC, MNC, true>;
 // dpre^T . X and dY^T . post: both operands are row-contiguous with k = token.
-using CfgDw = GemmCfg<2, 256, 256, 2, MNC, MNC>;
+using CfgDw = GemmCfg<2, 256, 128, 64, 2, 2, MNC, MNC, true>;
 
 struct BwdPlan {
   size_t dpre_bytes, part_bytes;
@@ -24,7 +24,8 @@ static BwdPlan bwd_plan(int64_t M, int64_t d, int64_t h) {
   BwdPlan p;
   p.dpre_bytes = align_up((size_t)(M * h) * 2, 256);
   const int64_t tiles = cdiv(h, CfgDw::BM) * cdiv(d, CfgDw::BN);
-  int64_t s = 256 / (tiles > 0 ? tiles : 1);
+  // about two rounds of blocks over 256 CUs x OCC resident blocks
+  int64_t s = (256 * CfgDw::OCC * 2 + tiles - 1) / (tiles > 0 ? tiles : 1) / 2;
   const int64_t max_s = cdiv(M, 512);
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
@@ -60,6 +61,7 @@ static int launch_reduce(const float* part, int splits, int64_t n, float* out, i
   const int64_t n4 = n / 4;
   int64_t blocks = cdiv(n4, 256);
   if (blocks > 4096) blocks = 4096;
+  TraceScope trace("splitk_reduce", st);
   hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)blocks), dim3(256), 0, st, (const float4*)part, splits, n4,
                      (float4*)out, accumulate);
   return launch_status();
@@ -70,21 +72,22 @@ static int launch_zero(float* out, int64_t n, hipStream_t st) {
   int64_t blocks = cdiv(n4, 256);
   if (blocks > 4096) blocks = 4096;
   if (blocks == 0) return FP8MLP_OK;
+  TraceScope trace("fill_zero", st);
   hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, st, (float4*)out, n4);
   return launch_status();
 }
 
 // One weight gradient C [Mo, No] = A^T B with A [K, Mo], B [K, No] (K = tokens).
-static int weight_grad(const uint16_t* A, int64_t Mo, const uint16_t* B, int64_t No, int64_t K, float* out,
+static int weight_grad(const char* name, const uint16_t* A, int64_t Mo, const uint16_t* B, int64_t No, int64_t K, float* out,
                        int accumulate, const BwdPlan& plan, float* part, hipStream_t st) {
   GemmArgs a{A, Mo, B, No, Mo, No, K, (int)cdiv(Mo, CfgDw::BM), (int)cdiv(No, CfgDw::BN), plan.splits,
              plan.k_per_split};
   if (plan.splits == 1) {
     EpiF32 epi{out, No, 0, accumulate};
-    return launch_gemm<CfgDw>(a, epi, st);
+    return launch_gemm<CfgDw>(name, a, epi, st);
   }
   EpiF32 epi{part, No, Mo * No, 0};
-  FP8MLP_TRY(launch_gemm<CfgDw>(a, epi, st));
+  FP8MLP_TRY(launch_gemm<CfgDw>(name, a, epi, st));
   return launch_reduce(part, plan.splits, Mo * No, out, accumulate, st);
 }
 
@@ -131,17 +134,17 @@ int mlp_relu2_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* W1, con
   {
     GemmArgs a{dY, d, W2, h, M, h, d, (int)cdiv(M, CfgDpost::BM), (int)cdiv(h, CfgDpost::BN), 1, d};
     EpiDpre epi{post, dpre, h};
-    FP8MLP_TRY(launch_gemm<CfgDpost>(a, epi, st));
+    FP8MLP_TRY(launch_gemm<CfgDpost>("dpost_gemm_dpre", a, epi, st));
   }
   // 2. dX = dpre W1
   {
     GemmArgs a{dpre, h, W1, d, M, d, h, (int)cdiv(M, CfgDx::BM), (int)cdiv(d, CfgDx::BN), 1, h};
-    EpiBf16Out epi{dX, d, 0, nullptr, 0.0f, nullptr, nullptr, nullptr};
-    FP8MLP_TRY(launch_gemm<CfgDx>(a, epi, st));
+    EpiBf16Out epi{dX, d, 0, nullptr, 0.0f, nullptr, nullptr};
+    FP8MLP_TRY(launch_gemm<CfgDx>("dx_gemm", a, epi, st));
   }
   // 3. dW1 = dpre^T X ; 4. dW2 = dY^T post
-  FP8MLP_TRY(weight_grad(dpre, h, X, d, M, dW1, accumulate, plan, part, st));
-  FP8MLP_TRY(weight_grad(dY, d, post, h, M, dW2, accumulate, plan, part, st));
+  FP8MLP_TRY(weight_grad("dw1_gemm", dpre, h, X, d, M, dW1, accumulate, plan, part, st));
+  FP8MLP_TRY(weight_grad("dw2_gemm", dY, d, post, h, M, dW2, accumulate, plan, part, st));
   return FP8MLP_OK;
 }
 

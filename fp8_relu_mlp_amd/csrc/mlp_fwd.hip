@@ -5,12 +5,13 @@
 
 namespace fp8mlp {
 
-// X [M,d] . W1[h,d]^T : both operands k-contiguous, 256 x 256 tiles.
-using CfgUp = GemmCfg<2, 256, 256, 2, KC, KC>;
+// X [M,d] . W1[h,d]^T : both operands k-contiguous; 256 x 256 tiles, one block per CU,
+// direct global -> LDS loads.
+using CfgUp = GemmCfg<2, 256, 256, 128, 2, 1, KC, KC>;
 // post_q [M,h] . W2t_q [h,d] : e4m3, the cache is read with transposing LDS loads.
-using CfgDown8 = GemmCfg<1, 192, 256, 2, KC, MNC>;
+using CfgDown8 = GemmCfg<1, 192, 128, 128, 2, 2, KC, MNC, true>;
 // post [M,h] . W2[d,h]^T : bf16 eval path.
-using CfgDownBf16 = GemmCfg<2, 192, 256, 2, KC, KC>;
+using CfgDownBf16 = GemmCfg<2, 192, 128, 64, 2, 2, KC, KC, true>;
 
 struct FwdPlan {
   int64_t tm, tn;          // up-projection tiles
@@ -71,7 +72,7 @@ int mlp_relu2_fwd(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t
   {
     GemmArgs a{X, d, W1, d, M, h, d, (int)plan.tm, (int)plan.tn, 1, d};
     EpiRelu2Quant epi{post, train ? post_q : nullptr, partial, amax_prev, margin, h, (int)plan.tn};
-    FP8MLP_TRY(launch_gemm<CfgUp>(a, epi, st));
+    FP8MLP_TRY(launch_gemm<CfgUp>("up_gemm_relu2_quant", a, epi, st));
   }
   // 2. reduce the partial amax tensor; record the scale that was used
   FP8MLP_TRY(launch_max_small(partial, plan.tm * plan.tn, amax_out, amax_prev, margin, train ? scale_out : nullptr,
@@ -79,12 +80,12 @@ int mlp_relu2_fwd(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t
   // 3. down-projection
   if (train) {
     GemmArgs a{post_q, h, W2t_q, d, M, d, h, (int)cdiv(M, CfgDown8::BM), (int)cdiv(d, CfgDown8::BN), 1, h};
-    EpiBf16Out epi{Y, d, 1, amax_prev, margin, nullptr, w2_inv_scale, nullptr};
-    FP8MLP_TRY(launch_gemm<CfgDown8>(a, epi, st));
+    EpiBf16Out epi{Y, d, 1, amax_prev, margin, nullptr, w2_inv_scale};
+    FP8MLP_TRY(launch_gemm<CfgDown8>("down_gemm_e4m3", a, epi, st));
   } else {
     GemmArgs a{post, h, W2, h, M, d, h, (int)cdiv(M, CfgDownBf16::BM), (int)cdiv(d, CfgDownBf16::BN), 1, h};
-    EpiBf16Out epi{Y, d, 0, nullptr, 0.0f, nullptr, nullptr, nullptr};
-    FP8MLP_TRY(launch_gemm<CfgDownBf16>(a, epi, st));
+    EpiBf16Out epi{Y, d, 0, nullptr, 0.0f, nullptr, nullptr};
+    FP8MLP_TRY(launch_gemm<CfgDownBf16>("down_gemm_bf16_eval", a, epi, st));
   }
   return FP8MLP_OK;
 }

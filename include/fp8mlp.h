@@ -178,15 +178,35 @@ int fp8_scale_from_amax(const float* amax, float margin, float* scale_out, float
  * fp8_linear -- forward of an FP8 projection ("NanoGPT Speedrun (Track 1)",
  * "Changes vs Record #83" item 1: QKV and output projections in e4m3 on the
  * forward pass, weights stored transposed):
- *   Xq = e4m3(fp32(X * *x_scale))        (quantised inside the GEMM, never stored)
+ *   Xq = e4m3(fp32(X * *x_scale))        (RNE, saturating; kept in the workspace)
  *   Y  = bf16((Xq . Wt_q) * fp32(1 / *x_scale) * *w_inv_scale)
  * X [M, K] bf16, Wt_q [K, N] e4m3 (from fp8_cast_transpose), Y [M, N] bf16.
  * x_scale, w_inv_scale: device fp32.  x_amax_out: device fp32 or NULL; if
  * given it receives max |X| (for the next step's delayed scale).
  * K: a positive multiple of 128, N: a positive multiple of 64; M >= 0.
+ * workspace: fp8_linear_workspace(M, K) bytes (the e4m3 copy of X).
  * ---------------------------------------------------------------------- */
+size_t fp8_linear_workspace(int64_t M, int64_t K);
 int fp8_linear(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, const float* w_inv_scale,
-               uint16_t* Y, float* x_amax_out, int64_t M, int64_t K, int64_t N, void* stream);
+               uint16_t* Y, float* x_amax_out, int64_t M, int64_t K, int64_t N, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Per-kernel timing (benchmarking / profiling aid, not part of the method).
+ * fp8mlp_timing_start(capacity) creates up to `capacity` hipEvent pairs
+ * (driver objects, no device memory) and, until fp8mlp_timing_stop(), brackets
+ * every kernel this library launches from the calling thread with
+ * hipEventRecord on that kernel's stream.  fp8mlp_timing_stop() returns the
+ * number of kernels recorded; launches beyond `capacity` are not recorded
+ * and are counted by fp8mlp_timing_dropped().  After the streams have been
+ * synchronised, fp8mlp_timing_get(i, &name, &ms) returns the i-th kernel's
+ * name (a static string) and duration in milliseconds.  State is per thread;
+ * a new fp8mlp_timing_start() discards the previous records.
+ * ---------------------------------------------------------------------- */
+int fp8mlp_timing_start(int capacity);
+int fp8mlp_timing_stop(void);
+int fp8mlp_timing_get(int i, const char** name, float* ms);
+int fp8mlp_timing_dropped(void);
 
 #ifdef __cplusplus
 }

@@ -109,6 +109,10 @@ def test_bwd_and_misc_validation(L):
     assert L.fp8_cast_transpose(16, 64, 64, 16, None, None, None, None, None, 0, None) == E_WS
     assert L.fp8_scale_from_amax(None, 2.0, None, None, None) == E_NULL
     assert L.fp8_scale_from_amax(16, -1.0, None, None, None) == E_ARG
-    assert L.fp8_linear(16, 16, 16, 16, 16, None, 100, 192, 256, None) == E_SHAPE   # K % 128
-    assert L.fp8_linear(16, None, 16, 16, 16, None, 100, 256, 256, None) == E_NULL
-    assert L.fp8_linear(16, 16, 16, 16, 17, None, 100, 256, 256, None) == E_ALIGN
+    lin = lambda **kw: L.fp8_linear(*dict(dict(X=16, xs=16, W=16, wi=16, Y=16, am=None, M=100, K=256, N=256,
+                                                ws=16, wsb=1 << 20, st=None), **kw).values())
+    assert lin(K=192) == E_SHAPE              # K % 128
+    assert lin(xs=None) == E_NULL
+    assert lin(Y=17) == E_ALIGN
+    assert lin(ws=None) == E_WS
+    assert lin(wsb=100) == E_WS

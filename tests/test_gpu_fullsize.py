@@ -1,0 +1,130 @@
+"""GPU parity at the full benchmark sizes, in the launch configuration the
+benchmark times (Relu2MLP: fwd TRAIN + bwd + W2 cache refresh).
+
+The oracle checks sampled outputs it can compute one by one (rows of post,
+post_q, Y, dX; rows of dW1; columns of dW2) plus properties over whole
+tensors (amax against the max of the GPU's full post).
+"""
+import numpy as np
+import pytest
+import torch
+
+from fp8_relu_mlp_amd import synth
+from oracle import formats as F
+from oracle import mlp as O
+
+from .gpu_helpers import DEV, bf16_dev, bits, case, f32_bits, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fm():
+    import fp8_relu_mlp_amd as fm
+    fm.lib()
+    return fm
+
+
+def _max_bf16_nonneg(b):
+    """max of non-negative bf16 values given as bits (unsigned order = value order)."""
+    return float(F.bf16_to_f64(np.uint16(b.max()))) if b.size else 0.0
+
+
+def test_fwdbwd_full_size_sampled(fm):
+    M, d, h = synth.WORKLOADS["fwdbwd"][:3]
+    seed = synth.WORKLOADS["fwdbwd"][3]
+    ins = synth.mlp_inputs(M, d, h, seed, with_dy=True)
+    case(f"full-size fwd+bwd M={M} d={d} h={h}")
+    blk = fm.Relu2MLP(bf16_dev(ins["W1"]), bf16_dev(ins["W2"]), margin=2.0, amax_init=1.0)
+    X, dY = bf16_dev(ins["X"]), bf16_dev(ins["dY"])
+    blk.forward(X)                                   # bootstrap amax_prev
+    amax_prev = float(blk.amax_prev.item())
+    Y, post, post_q = blk.forward(X)
+    dX, dW1, dW2 = blk.backward(dY, X, post)
+    torch.cuda.synchronize()
+    post_b = bits(post)
+    # amax: bit-exact over the whole tensor
+    assert f32_bits(blk.amax_last.item()) == f32_bits(_max_bf16_nonneg(post_b))
+    s = O.delayed_scale(amax_prev, 2.0)
+    assert f32_bits(blk.scale_used.item()) == f32_bits(s)
+    rows = np.random.default_rng(1).choice(M, size=48, replace=False)
+    rows.sort()
+    rows = np.concatenate([rows, [0, M - 1]])
+    pq = post_q.cpu().numpy()[rows]
+    pb = post_b[rows]
+    # codes bit-exact given the GPU's post (sampled rows)
+    assert (O.quantize(F.bf16_to_f64(pb), s) == pq).all()
+    W2t, _, inv_sw, _ = O.cast_transpose(ins["W2"])
+    assert (W2t == blk.W2t_q.cpu().numpy()).all()
+    ref = O.mlp_fwd(ins["X"][rows], ins["W1"], W2t, inv_sw, amax_prev, 2.0)
+    assert rel_fro(F.bf16_to_f64(pb), F.bf16_to_f64(ref["post"])) < 1e-2
+    y = F.bf16_to_f64(bits(Y)[rows])
+    assert rel_fro(y, F.bf16_to_f64(ref["y"])) < 2e-2
+    assert rel_fro(y, O.down_fp8(pq, W2t, O.inv_scale(s), inv_sw)) < 4e-3
+    # backward on sampled rows / columns, fed the GPU's post
+    post_f = F.bf16_to_f64(post_b)
+    r1 = [0, 1234, h - 1]
+    c2 = [0, 777, h - 1]
+    bs = O.mlp_bwd_sampled(ins["dY"], ins["X"], ins["W1"], ins["W2"], post_f, rows, r1, c2)
+    assert rel_fro(F.bf16_to_f64(bits(dX)[rows]), bs["dX_rows"]) < 4e-3
+    assert rel_fro(dW1.cpu().numpy()[r1].astype(np.float64), bs["dW1_rows"]) < 4e-3
+    assert rel_fro(dW2.cpu().numpy()[:, c2].astype(np.float64), bs["dW2_cols"]) < 1e-4
+
+
+def test_fwd_two_steps_full_size(fm):
+    """Two-step forward at M=16384 with the W1 perturbation between steps."""
+    M, d, h = synth.WORKLOADS["fwd2"][:3]
+    seed = synth.WORKLOADS["fwd2"][3]
+    ins = synth.mlp_inputs(M, d, h, seed)
+    case(f"two-step forward M={M}")
+    blk = fm.Relu2MLP(bf16_dev(ins["W1"]), bf16_dev(ins["W2"]), margin=2.0, amax_init=1.0)
+    X = bf16_dev(ins["X"])
+    blk.forward(X)
+    a0 = float(blk.amax_prev.item())
+    blk.forward(X)                                   # step 1 with its own exact amax
+    a1 = float(blk.amax_prev.item())
+    assert a1 == a0
+    W1b = synth.perturbed_w1(ins["W1"], seed)
+    X2 = synth.mlp_inputs(M, d, h, seed, step=1)["X"]
+    blk.W1 = bf16_dev(W1b)
+    Y, post, post_q = blk.forward(bf16_dev(X2))      # step 2 uses step 1's amax
+    torch.cuda.synchronize()
+    assert f32_bits(blk.scale_used.item()) == f32_bits(O.delayed_scale(a1, 2.0))
+    post_b = bits(post)
+    assert f32_bits(blk.amax_last.item()) == f32_bits(_max_bf16_nonneg(post_b))
+    s = O.delayed_scale(a1, 2.0)
+    # every code of step 2, bit-exact given the GPU's post
+    pq = post_q.cpu().numpy()
+    for r0 in range(0, M, 4096):
+        assert (O.quantize(F.bf16_to_f64(post_b[r0:r0 + 4096]), s) == pq[r0:r0 + 4096]).all()
+    rows = np.arange(0, M, 257)
+    W2t, _, inv_sw, _ = O.cast_transpose(ins["W2"])
+    ref = O.mlp_fwd(X2[rows], W1b, W2t, inv_sw, a1, 2.0)
+    assert rel_fro(F.bf16_to_f64(bits(Y)[rows]), F.bf16_to_f64(ref["y"])) < 2e-2
+
+
+@pytest.mark.parametrize("which", ["qkv", "o"])
+def test_fp8_linear_full_size(fm, which):
+    a = synth.attn_inputs()
+    Xb = a["X"] if which == "qkv" else a["Xo"]
+    Wb = a["Wqkv"] if which == "qkv" else a["Wo"]
+    M, K = Xb.shape
+    N = Wb.shape[0]
+    case(f"fp8_linear full size {which} M={M} K={K} N={N}")
+    X, W = bf16_dev(Xb), bf16_dev(Wb)
+    Wt = torch.empty((K, N), dtype=torch.uint8, device=DEV)
+    inv_w = torch.zeros(1, dtype=torch.float32, device=DEV)
+    fm.fp8_cast_transpose(W, Wt, inv_scale_out=inv_w)
+    amax = torch.zeros(1, dtype=torch.float32, device=DEV)
+    fm.amax_reduce(X, amax)
+    sx = torch.zeros(1, dtype=torch.float32, device=DEV)
+    fm.fp8_scale_from_amax(amax, 1.0, sx)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    fm.fp8_linear(X, sx, Wt, inv_w, Y)
+    torch.cuda.synchronize()
+    assert f32_bits(amax.item()) == f32_bits(O.amax(F.bf16_to_f64(Xb)))
+    rows = np.arange(0, M, 997)
+    Wt_o, _, inv_o, _ = O.cast_transpose(Wb)
+    assert (Wt_o == Wt.cpu().numpy()).all()
+    ref = F.bf16_to_f64(O.fp8_linear(Xb[rows], float(sx.item()), Wt_o, inv_o))
+    assert rel_fro(F.bf16_to_f64(bits(Y)[rows]), ref) < 4e-3

@@ -1,0 +1,92 @@
+"""GPU parity of fp8_linear (FP8 QKV / output projections) against the oracle.
+
+Gates: Y within relative Frobenius 2e-2 of the oracle (an e4m3 GEMM is in its
+lineage) and, since the GPU quantises X with the same fp32 product and RNE
+encode as the oracle, within the bf16 output rounding (4e-3) as well; the
+optional amax of X is bit-exact; the ternary special case is exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+from fp8_relu_mlp_amd import synth
+from oracle import formats as F
+from oracle import mlp as O
+
+from .gpu_helpers import DEV, bf16_dev, bits, case, f32_bits, f32_dev, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fm():
+    import fp8_relu_mlp_amd as fm
+    fm.lib()
+    return fm
+
+
+def run_linear(fm, Xb, Wb, margin=1.0, scale_in=None):
+    """Exact per-tensor scales: amax_reduce + fp8_scale_from_amax for X,
+    fp8_cast_transpose (exact policy) for W; returns GPU outputs."""
+    M, K = Xb.shape
+    N = Wb.shape[0]
+    X, W = bf16_dev(Xb), bf16_dev(Wb)
+    Wt = torch.empty((K, N), dtype=torch.uint8, device=DEV)
+    inv_w = f32_dev(0.0)
+    if scale_in is None:
+        fm.fp8_cast_transpose(W, Wt, inv_scale_out=inv_w)
+    else:
+        fm.fp8_cast_transpose(W, Wt, scale_in=f32_dev(scale_in), inv_scale_out=inv_w)
+    amax = f32_dev(0.0)
+    fm.amax_reduce(X, amax)
+    sx = f32_dev(0.0)
+    fm.fp8_scale_from_amax(amax, margin, sx)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    xam = f32_dev(-1.0)
+    fm.fp8_linear(X, sx, Wt, inv_w, Y, xam)
+    torch.cuda.synchronize()
+    return {"Y": bits(Y), "sx": sx.item(), "inv_w": inv_w.item(), "Wt": Wt.cpu().numpy(), "xamax": xam.item()}
+
+
+@pytest.mark.parametrize("M,K,N", [(1000, 768, 2304), (777, 768, 768), (1, 128, 64), (300, 256, 192)])
+def test_fp8_linear_parity(fm, M, K, N):
+    case(f"fp8_linear M={M} K={K} N={N}")
+    a = synth.attn_inputs(M=M, d=K, qkv=N, seed=90 + M)
+    g = run_linear(fm, a["X"], a["Wqkv"])
+    Xf = F.bf16_to_f64(a["X"])
+    assert f32_bits(g["xamax"]) == f32_bits(O.amax(Xf))
+    sx = O.exact_scale(O.amax(Xf))
+    assert f32_bits(g["sx"]) == f32_bits(sx)
+    Wt, _, inv_w, _ = O.cast_transpose(a["Wqkv"])
+    assert (Wt == g["Wt"]).all()
+    ref = F.bf16_to_f64(O.fp8_linear(a["X"], sx, Wt, inv_w))
+    Y = F.bf16_to_f64(g["Y"])
+    assert rel_fro(Y, ref) < 4e-3
+    assert rel_fro(Y, ref) < 2e-2
+    # sanity against the unquantised product: two e4m3 roundings with an RMS
+    # relative error of about 0.03 each give about 0.04; allow twice that
+    exact = Xf @ F.bf16_to_f64(a["Wqkv"]).T
+    assert rel_fro(Y, exact) < 0.08
+
+
+def test_fp8_linear_lossless(fm):
+    M, K, N = 500, 256, 128
+    X = synth.ternary_bf16((M, K), 5, "X")
+    W = synth.ternary_bf16((N, K), 5, "W")
+    case("fp8_linear lossless ternary")
+    g = run_linear(fm, X, W, margin=448.0, scale_in=1.0)      # scale 448/(448*1) = 1
+    assert g["sx"] == 1.0
+    y = F.bf16_to_f64(X).astype(np.int64) @ F.bf16_to_f64(W).astype(np.int64).T
+    assert np.abs(y).max() <= 256
+    assert (F.bf16_to_f64(g["Y"]) == y).all()
+
+
+def test_fp8_linear_empty(fm):
+    case("fp8_linear M=0")
+    X = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    Wt = torch.zeros((256, 128), dtype=torch.uint8, device=DEV)
+    Y = torch.empty((0, 128), dtype=torch.bfloat16, device=DEV)
+    am = f32_dev(5.0)
+    fm.fp8_linear(X, f32_dev(1.0), Wt, f32_dev(1.0), Y, am)
+    torch.cuda.synchronize()
+    assert am.item() == 0.0
