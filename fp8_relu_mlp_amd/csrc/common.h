@@ -49,6 +49,35 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
   return (uint32_t)w;
 }
 
+// e4m3 codes of four values that are >= +0 or NaN (byte 0 = a).  The
+// converter rounds to nearest even and already gives 0x7E on (448, 464];
+// above 464 and at +inf it gives 0x7F, which is rewritten to 0x7E
+// (saturation), while a NaN input gives 0xFF and stays a NaN code.  Cheaper
+// than clamping each value before the conversion.
+__device__ __forceinline__ uint32_t pack_e4m3x4_nonneg(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  const uint32_t u = (uint32_t)w;
+  const uint32_t m = u ^ 0x7f7f7f7fu;                        // bytes that were 0x7F are now 0
+  const uint32_t nz = ((m & 0x7f7f7f7fu) + 0x7f7f7f7fu) | m;  // bit 7 of a byte: byte != 0
+  const uint32_t z = ~nz & 0x80808080u;                      // bit 7 of a byte: code was 0x7F
+  return u - (z >> 7);                                        // 0x7F -> 0x7E, no borrow
+}
+
+// Keeps the compiler from re-deriving a value from its operands (the packed
+// bf16 word below would otherwise be re-converted value by value).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// relu(a)^2 with NaN kept and -inf sent to 0: IEEE maximum(a, +0) (NaN
+// propagating, one v_maximum3_f32 on gfx950) then a square.
+__device__ __forceinline__ float relu_sq(float a) {
+  const float r = __builtin_elementwise_maximum(a, 0.0f);
+  return r * r;
+}
+
 // Running max of |x| over two packed bf16 values, on fp32 bit patterns.
 __device__ __forceinline__ uint32_t max_abs_bf16x2(uint32_t m, uint32_t w) {
   const uint32_t a0 = (w & 0x7fffu) << 16, a1 = (w >> 16 & 0x7fffu) << 16;

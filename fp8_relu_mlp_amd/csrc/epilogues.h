@@ -14,8 +14,9 @@ namespace fp8mlp {
 //   post   = bf16(relu(pre)^2)
 //   post_q = e4m3(fp32(post * scale)),  scale from amax(t-1) and the margin
 //   partial[tile] = max(post over the tile)
-// relu keeps NaN (pre < 0 ? 0 : pre) and the maximum is taken on bit
-// patterns, so a NaN anywhere reaches amax.
+// relu keeps NaN and the maximum is taken on bit patterns, so a NaN anywhere
+// reaches amax; post >= +0, so the e4m3 encode uses the non-negative fast
+// path.
 struct EpiRelu2Quant {
   uint16_t* post;
   uint8_t* post_q;        // nullptr: no quantised copy (eval)
@@ -40,9 +41,7 @@ struct EpiRelu2Quant {
         float pv[16];
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
-          const float a0 = acc[fm][fn][e], a1 = acc[fm][fn][e + 1];
-          const float r0 = a0 < 0.0f ? 0.0f : a0, r1 = a1 < 0.0f ? 0.0f : a1;
-          pk[e / 2] = pack_bf16x2(r0 * r0, r1 * r1);
+          pk[e / 2] = opaque(pack_bf16x2(relu_sq(acc[fm][fn][e]), relu_sq(acc[fm][fn][e + 1])));
           pv[e] = bf16_lo(pk[e / 2]);
           pv[e + 1] = bf16_hi(pk[e / 2]);
         }
@@ -52,10 +51,10 @@ struct EpiRelu2Quant {
           *(uint4*)(dst + 8) = uint4{pk[4], pk[5], pk[6], pk[7]};
           if (post_q) {
             uint4 q;
-            q.x = pack_e4m3x4(pv[0] * s, pv[1] * s, pv[2] * s, pv[3] * s);
-            q.y = pack_e4m3x4(pv[4] * s, pv[5] * s, pv[6] * s, pv[7] * s);
-            q.z = pack_e4m3x4(pv[8] * s, pv[9] * s, pv[10] * s, pv[11] * s);
-            q.w = pack_e4m3x4(pv[12] * s, pv[13] * s, pv[14] * s, pv[15] * s);
+            q.x = pack_e4m3x4_nonneg(pv[0] * s, pv[1] * s, pv[2] * s, pv[3] * s);
+            q.y = pack_e4m3x4_nonneg(pv[4] * s, pv[5] * s, pv[6] * s, pv[7] * s);
+            q.z = pack_e4m3x4_nonneg(pv[8] * s, pv[9] * s, pv[10] * s, pv[11] * s);
+            q.w = pack_e4m3x4_nonneg(pv[12] * s, pv[13] * s, pv[14] * s, pv[15] * s);
             *(uint4*)(post_q + m * ld + n) = q;
           }
 #pragma unroll
@@ -159,7 +158,8 @@ struct EpiDpre {
         uint32_t o[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-          const float r0 = sqrtf(bf16_lo(pw[i])), r1 = sqrtf(bf16_hi(pw[i]));
+          // v_sqrt_f32 (within 1 ulp of fp32) is far below the bf16 rounding of dpre
+          const float r0 = __builtin_amdgcn_sqrtf(bf16_lo(pw[i])), r1 = __builtin_amdgcn_sqrtf(bf16_hi(pw[i]));
           o[i] = pack_bf16x2((2.0f * r0) * acc[fm][fn][2 * i], (2.0f * r1) * acc[fm][fn][2 * i + 1]);
         }
         uint16_t* dst = dpre + m * ld + n;

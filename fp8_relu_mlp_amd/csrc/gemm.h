@@ -35,12 +35,14 @@ namespace fp8mlp {
 
 enum { KC = 0, MNC = 1 };
 
-template <int ELT_, int BM_, int BN_, int RB_, int STAGES_, int OCC_, int QL_, int PL_, bool REG_ = false>
+template <int ELT_, int BM_, int BN_, int RB_, int STAGES_, int OCC_, int QL_, int PL_, int REG_ = 0>
 struct GemmCfg {
   static constexpr int ELT = ELT_;                 // bytes per element: 2 bf16, 1 e4m3
-  // REG: tiles go global -> VGPRs -> LDS (buffer_load_dwordx4 + ds_write_b128,
-  // one tile held in registers); otherwise global -> LDS directly.
-  static constexpr bool REG = REG_;
+  // REG == 1: tiles go global -> VGPRs -> LDS (buffer_load_dwordx4 +
+  // ds_write_b128), the next tile waiting in registers while the current one
+  // is computed; REG == 0: global -> LDS directly (buffer_load ... lds) with
+  // STAGES LDS buffers.
+  static constexpr int REG = REG_;
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int RB = RB_;                   // bytes of k per tile row
   static constexpr int CPR = RB / 16;              // 16-byte chunks per k-contiguous row
@@ -68,7 +70,7 @@ struct GemmCfg {
   static_assert(PL == KC || (BN * ELT) % (ELT == 2 ? 256 : 128) == 0, "row-contiguous P tile rows");
   static_assert(LDS_BYTES * OCC <= 160 * 1024, "LDS");
   static_assert(LOADS * (STAGES - 2) < 64, "vmcnt");
-  static_assert(!REG || STAGES == 2, "register staging keeps one tile in flight");
+  static_assert(REG == 0 || (REG == 1 && STAGES == 2), "register staging: two LDS buffers, one register set");
 };
 
 struct GemmArgs {
@@ -80,6 +82,7 @@ struct GemmArgs {
   int tiles_m, tiles_n, splits;
   int64_t k_per_split;  // multiple of BK
   int stagger;          // > 0: blocks of the second residency slot start ~stagger x 4 us late
+  int group_m;          // tile rows per group of the tile order (set by launch_gemm)
 };
 
 // Per-block tile coordinates handed to the epilogue.
@@ -191,11 +194,21 @@ __global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) 
     for (int i = 0; i < a.stagger; i++) __builtin_amdgcn_s_sleep(127);
   }
 
-  // ---- tile assignment (XCD-aware; split fastest, then n, then m)
+  // ---- tile assignment.  Consecutive blocks go round-robin over the 8 XCDs;
+  // xcd_remap gives each XCD a contiguous run of logical tiles.  Logical
+  // order: split-k index slowest (blocks of one split share their k-range of
+  // both operands), then groups of GROUP_M tile rows, inside a group the row
+  // fastest, so the tiles an XCD runs at once form a near-square window that
+  // shares few A- and B-slabs in that XCD's L2.
+  const int GROUP_M = a.group_m;
   int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int split = t % a.splits;
-  t /= a.splits;
-  const int tn = t % a.tiles_n, tm = t / a.tiles_n;
+  const int per_split = a.tiles_m * a.tiles_n;
+  const int split = t / per_split;
+  t -= split * per_split;
+  const int per_group = GROUP_M * a.tiles_n;
+  const int grp = t / per_group, rem = t - grp * per_group;
+  const int gm = min(GROUP_M, a.tiles_m - grp * GROUP_M);
+  const int tm = grp * GROUP_M + rem % gm, tn = rem / gm;
   const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
   const int64_t kb = (int64_t)split * a.k_per_split;
   const int64_t ke = min(a.K, kb + a.k_per_split);
@@ -229,22 +242,26 @@ __global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) 
   const uint32_t qstep = C::QL == KC ? (uint32_t)C::RB : (uint32_t)(C::BK * ldq_b);
   const uint32_t pstep = C::PL == KC ? (uint32_t)C::RB : (uint32_t)(C::BK * ldp_b);
 
-  // register staging: one tile in flight in VGPRs
-  i32x4 rq_regs[C::REG ? C::Q_LOADS : 1], rp_regs[C::REG ? C::P_LOADS : 1];
-  auto gload = [&](int kt) {
+  // register staging: the next tile in flight in VGPRs
+  i32x4 rq_regs[1][C::REG ? C::Q_LOADS : 1], rp_regs[1][C::REG ? C::P_LOADS : 1];
+  auto gload = [&](int kt, int slot) {
     const uint32_t dq = (uint32_t)kt * qstep, dp = (uint32_t)kt * pstep;
 #pragma unroll
-    for (int j = 0; j < C::Q_LOADS; j++) rq_regs[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff[j] + dq, 0, 0);
+    for (int j = 0; j < C::Q_LOADS; j++)
+      rq_regs[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff[j] + dq, 0, 0);
 #pragma unroll
-    for (int j = 0; j < C::P_LOADS; j++) rp_regs[j] = __builtin_amdgcn_raw_buffer_load_b128(rp, poff[j] + dp, 0, 0);
+    for (int j = 0; j < C::P_LOADS; j++)
+      rp_regs[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(rp, poff[j] + dp, 0, 0);
   };
-  auto dswrite = [&](int stage) {
+  auto dswrite = [&](int stage, int slot) {
     FP8MLP_LDS char* sq = smem + stage * C::STAGE_BYTES;
     FP8MLP_LDS char* sp = sq + C::Q_BYTES;
 #pragma unroll
-    for (int j = 0; j < C::Q_LOADS; j++) *(FP8MLP_LDS i32x4*)(sq + ((j * 4 + wave) * 64 + lane) * 16) = rq_regs[j];
+    for (int j = 0; j < C::Q_LOADS; j++)
+      *(FP8MLP_LDS i32x4*)(sq + ((j * 4 + wave) * 64 + lane) * 16) = rq_regs[slot][j];
 #pragma unroll
-    for (int j = 0; j < C::P_LOADS; j++) *(FP8MLP_LDS i32x4*)(sp + ((j * 4 + wave) * 64 + lane) * 16) = rp_regs[j];
+    for (int j = 0; j < C::P_LOADS; j++)
+      *(FP8MLP_LDS i32x4*)(sp + ((j * 4 + wave) * 64 + lane) * 16) = rp_regs[slot][j];
   };
 
   auto issue = [&](int kt, int stage) {
@@ -361,15 +378,15 @@ __global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) 
   };
 
   // ---- main loop: one barrier per tile
-  if constexpr (C::REG) {
-    // tile kt+1 waits in registers while tile kt is computed from LDS; it is
-    // written to the other LDS buffer at the end of the iteration, and the
-    // loads of tile kt+2 are issued right after
+  if constexpr (C::REG > 0) {
+    // tile kt+1 waits in registers while tile kt is computed from LDS; at the
+    // end of the iteration it goes to the other LDS buffer and the registers
+    // are refilled with tile kt+2
     if (KT > 0) {
-      gload(0);
+      gload(0, 0);
       wait_vmcnt<0>();
-      dswrite(0);
-      if (KT > 1) gload(1);
+      dswrite(0, 0);
+      if (KT > 1) gload(1, 0);
     }
   } else {
 #pragma unroll
@@ -377,8 +394,8 @@ __global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) 
       if (s < KT) issue(s, s);
   }
 
-  for (int kt = 0; kt < KT; kt++) {
-    if constexpr (!C::REG) {
+  auto ktile = [&](int kt) {
+    if constexpr (C::REG == 0) {
       if (kt + C::STAGES - 2 < KT) {
         wait_vmcnt<C::LOADS * (C::STAGES - 2)>();
       } else {
@@ -386,7 +403,7 @@ __global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) 
       }
     }
     __syncthreads();
-    if constexpr (!C::REG) {
+    if constexpr (C::REG == 0) {
       if (kt + C::STAGES - 1 < KT) issue(kt + C::STAGES - 1, (kt + C::STAGES - 1) % C::STAGES);
     }
 
@@ -414,14 +431,15 @@ __global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) 
         for (int fn = 0; fn < C::FN; fn++) acc[fm][fn] = mma(pf[s & 1][fn], qf[s & 1][fm], acc[fm][fn]);
     }
     sched_tile<C::FM * C::FN, NREADS, C::SL>();
-    if constexpr (C::REG) {
+    if constexpr (C::REG > 0) {
       if (kt + 1 < KT) {
         wait_vmcnt<0>();
-        dswrite((kt + 1) & 1);
-        if (kt + 2 < KT) gload(kt + 2);
+        dswrite((kt + 1) & 1, 0);
+        if (kt + 2 < KT) gload(kt + 2, 0);
       }
     }
-  }
+  };
+  for (int kt = 0; kt < KT; kt++) ktile(kt);
 
   TileCtx ctx{m0, n0, tm, tn, split, wm, wn, lane, a.M, a.N};
   epi.template run<C>(ctx, acc, smem);

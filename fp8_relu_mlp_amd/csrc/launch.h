@@ -6,10 +6,25 @@
 
 namespace fp8mlp {
 
+// Tile rows per group of the tile order: the ~32 x OCC tiles an XCD runs at
+// once should form a near-square window of the tile grid (whole rows when the
+// grid is narrow), so they share as few operand slabs as possible.
+inline int tile_group_m(int tiles_m, int tiles_n, int occ) {
+  const int window = 32 * occ;
+  int side = 1;
+  while ((side + 1) * (side + 1) <= window) side++;
+  int g = tiles_n <= side ? window / (tiles_n > 0 ? tiles_n : 1) : side;
+  if (g < 1) g = 1;
+  if (g > tiles_m) g = tiles_m > 0 ? tiles_m : 1;
+  return g;
+}
+
 template <class C, class Epi>
-inline int launch_gemm(const char* name, const GemmArgs& a, const Epi& epi, hipStream_t st) {
-  const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n * a.splits;
+inline int launch_gemm(const char* name, const GemmArgs& args, const Epi& epi, hipStream_t st) {
+  const int64_t blocks = (int64_t)args.tiles_m * args.tiles_n * args.splits;
   if (blocks == 0) return FP8MLP_OK;
+  GemmArgs a = args;
+  a.group_m = tile_group_m(a.tiles_m, a.tiles_n, C::OCC);
   TraceScope trace(name, st);
   hipLaunchKernelGGL((gemm_kernel<C, Epi>), dim3((unsigned)blocks), dim3(256), 0, st, a, epi);
   return launch_status();

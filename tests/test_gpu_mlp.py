@@ -251,3 +251,29 @@ def test_fwd_bwd_deterministic(fm):
         outs.append((g["post"], g["post_q"], g["y"], g["amax"], dX, dW1, dW2))
     for a, b in zip(*outs):
         assert np.array_equal(np.asarray(a), np.asarray(b))
+
+
+def test_fwd_nonfinite_inputs(fm):
+    """inf / NaN in X: post becomes inf or NaN, the e4m3 copy saturates inf to
+    448 (0x7E) and keeps NaN a NaN code, and amax turns NaN (NaN propagates
+    through relu and the max)."""
+    M, d, h = 128, 64, 128
+    ins = synth.mlp_inputs(M, d, h, 54)
+    X = ins["X"].copy()
+    X[3, 0] = 0x7F80            # one +inf: row 3 of pre is +-inf, relu -> inf or 0
+    X[7, 5] = 0x7FC0            # one NaN: row 7 of pre is NaN everywhere
+    ins = dict(ins, X=X)
+    case("fwd non-finite inputs")
+    g = run_fwd(fm, ins, amax_prev=2.0)
+    post = F.bf16_to_f64(g["post"])
+    ref_post = O.up_relu2(X, ins["W1"])
+    assert np.isinf(ref_post).any() and (ref_post[3] == 0).any()
+    assert np.array_equal(np.isnan(post), np.isnan(ref_post))
+    assert np.array_equal(np.isinf(post), np.isinf(ref_post))
+    assert np.isnan(g["amax"])
+    s = O.delayed_scale(2.0, 2.0)
+    ref_q = O.quantize(post, s)
+    from .gpu_helpers import same_codes
+    assert same_codes(g["post_q"], ref_q)
+    assert (g["post_q"][np.isinf(post)] == 0x7E).all()
+    assert ((g["post_q"][np.isnan(post)] & 0x7F) == 0x7F).all()
