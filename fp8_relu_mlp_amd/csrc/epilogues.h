@@ -6,6 +6,75 @@
 
 namespace fp8mlp {
 
+// ------------------------------------------------------------------ LDS staging
+// In the accumulator layout one store instruction of a wave touches 32 rows;
+// 16-bit results therefore go through LDS and leave row by row: 16 bytes per
+// lane, 8 lanes per 128-byte line.  LDS image of the BM x BN tile: rows of
+// BN/8 chunks of 16 bytes, the chunk index XOR-ed with the row's low bits, so
+// the fragment-order writes (16 lanes = 16 consecutive rows, one chunk) and
+// the row-order reads (16 lanes = 16 chunks of one row) both use 16 distinct
+// 16-byte bank groups.
+template <class C>
+struct Tile16 {
+  static constexpr int CPR = C::BN / 8;                    // 16-byte chunks per row
+  static constexpr int XM = CPR < 16 ? CPR - 1 : 15;
+  static constexpr int BYTES = C::BM * C::BN * 2;
+  static constexpr int PASSES = C::BM * CPR / 256;         // row-order passes of the block
+  static_assert((C::BM * CPR) % 256 == 0, "row-order passes");
+  __device__ static __forceinline__ uint32_t off(int row, int chunk) {
+    return (uint32_t)(row * CPR + (chunk ^ (row & XM))) * 16u;
+  }
+  // first chunk of fragment (fm, fn) held by this lane and its row
+  __device__ static __forceinline__ int frag_row(const TileCtx& c, int fm) { return c.wm * C::WTM + fm * 32 + (c.lane & 31); }
+  __device__ static __forceinline__ int frag_chunk(const TileCtx& c, int fn) {
+    return (c.wn * C::WTN + fn * 32) / 8 + (C::PERM ? 2 * (c.lane >> 5) : 0);
+  }
+  // 16 values of fragment (fm, fn), packed in pairs, into the LDS image
+  __device__ static __forceinline__ void put(FP8MLP_LDS char* s, const TileCtx& c, int fm, int fn, const uint32_t (&w)[8]) {
+    const int row = frag_row(c, fm), ch = frag_chunk(c, fn);
+    if constexpr (C::PERM) {
+      *(FP8MLP_LDS i32x4*)(s + off(row, ch)) = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+      *(FP8MLP_LDS i32x4*)(s + off(row, ch + 1)) = i32x4{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+    } else {
+      // four runs of 4 columns at 8g + 4h: half a chunk each
+#pragma unroll
+      for (int g = 0; g < 4; g++)
+        *(FP8MLP_LDS i32x2*)(s + off(row, ch + g) + 8 * (c.lane >> 5)) = i32x2{(int)w[2 * g], (int)w[2 * g + 1]};
+    }
+  }
+  // Row-order sweep: f(m, n, 16 bytes) for every chunk inside the matrix.
+  template <class F>
+  __device__ static __forceinline__ void rows(const FP8MLP_LDS char* s, const TileCtx& c, F&& f) {
+#pragma unroll
+    for (int p = 0; p < PASSES; p++) {
+      const int i = p * 256 + (int)threadIdx.x;
+      const int row = i / CPR, ch = i % CPR;
+      const i32x4 r = lds_read_b128(s, off(row, ch));
+      const uint4 v{(uint32_t)r[0], (uint32_t)r[1], (uint32_t)r[2], (uint32_t)r[3]};
+      const int64_t m = c.m0 + row, n = c.n0 + ch * 8;
+      if (m < c.M && n < c.N) f(m, n, v);
+    }
+  }
+  // Global 16-bit matrix (leading dimension ld) -> LDS image, loaded straight
+  // into LDS in row order; rows past the matrix end read as zero.
+  __device__ static __forceinline__ void load(FP8MLP_LDS char* s, const TileCtx& c, const uint16_t* g, int64_t ld) {
+    const uint16_t* base = g + c.m0 * ld + c.n0;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (uint64_t)((c.M - c.m0) * ld - c.n0) * 2u);
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int p = 0; p < PASSES; p++) {
+      const int i = (p * 4 + wave) * 64 + c.lane;   // LDS-linear chunk this lane fills
+      const int row = i / CPR, ch = (i % CPR) ^ (row & XM);
+      buffer_load_lds16(r, s + (p * 4 + wave) * 1024, (uint32_t)(row * ld * 2 + ch * 16));
+    }
+  }
+};
+
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+  typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+
 // Up-projection epilogue ("A Retrospective on Our World Records", Main
 // Track: while the fused up-projection kernel holds the post-activation in
 // registers it writes the BF16 tensor for backward, emits the FP8 version and
@@ -14,9 +83,9 @@ namespace fp8mlp {
 //   post   = bf16(relu(pre)^2)
 //   post_q = e4m3(fp32(post * scale)),  scale from amax(t-1) and the margin
 //   partial[tile] = max(post over the tile)
-// relu keeps NaN and the maximum is taken on bit patterns, so a NaN anywhere
-// reaches amax; post >= +0, so the e4m3 encode uses the non-negative fast
-// path.
+// post is >= +0 or NaN, so its bf16 bit patterns order like the values (NaN
+// above +inf): the tile maximum is a max of 16-bit patterns and a NaN reaches
+// amax.  The e4m3 copy is made from the staged bf16 values on the way out.
 struct EpiRelu2Quant {
   uint16_t* post;
   uint8_t* post_q;        // nullptr: no quantised copy (eval)
@@ -27,53 +96,48 @@ struct EpiRelu2Quant {
   int tiles_n;
 
   template <class C>
+  static constexpr int lds_bytes() { return Tile16<C>::BYTES + 16; }
+
+  template <class C>
   __device__ __forceinline__ void run(const TileCtx& c, f32x16 (&acc)[C::FM][C::FN], FP8MLP_LDS char* smem) {
     static_assert(C::PERM, "needs 16 consecutive columns per lane");
+    using T = Tile16<C>;
     const float s = post_q ? scale_from_amax(*amax_prev, margin) : 1.0f;
-    uint32_t mx = 0;
+    uint32_t mx = 0;   // two running 16-bit maxima
+    __syncthreads();   // every wave is done with the last pipeline stage
 #pragma unroll
     for (int fm = 0; fm < C::FM; fm++) {
-      const int64_t m = c.m0 + epi_row<C>(c, fm);
+      const bool row_in = c.m0 + T::frag_row(c, fm) < c.M;
 #pragma unroll
       for (int fn = 0; fn < C::FN; fn++) {
-        const int64_t n = c.n0 + epi_col<C>(c, fn, 0);
         uint32_t pk[8];
-        float pv[16];
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          pk[e / 2] = opaque(pack_bf16x2(relu_sq(acc[fm][fn][e]), relu_sq(acc[fm][fn][e + 1])));
-          pv[e] = bf16_lo(pk[e / 2]);
-          pv[e + 1] = bf16_hi(pk[e / 2]);
-        }
-        if (m < c.M && n < c.N) {
-          uint16_t* dst = post + m * ld + n;
-          *(uint4*)dst = uint4{pk[0], pk[1], pk[2], pk[3]};
-          *(uint4*)(dst + 8) = uint4{pk[4], pk[5], pk[6], pk[7]};
-          if (post_q) {
-            uint4 q;
-            q.x = pack_e4m3x4_nonneg(pv[0] * s, pv[1] * s, pv[2] * s, pv[3] * s);
-            q.y = pack_e4m3x4_nonneg(pv[4] * s, pv[5] * s, pv[6] * s, pv[7] * s);
-            q.z = pack_e4m3x4_nonneg(pv[8] * s, pv[9] * s, pv[10] * s, pv[11] * s);
-            q.w = pack_e4m3x4_nonneg(pv[12] * s, pv[13] * s, pv[14] * s, pv[15] * s);
-            *(uint4*)(post_q + m * ld + n) = q;
-          }
+        for (int e = 0; e < 16; e += 2) pk[e / 2] = pack_bf16x2(relu_sq(acc[fm][fn][e]), relu_sq(acc[fm][fn][e + 1]));
+        if (row_in && c.n0 + T::frag_chunk(c, fn) * 8 < c.N) {
 #pragma unroll
-          for (int e = 0; e < 16; e++) {
-            const uint32_t b = __float_as_uint(pv[e]);
-            mx = b > mx ? b : mx;
-          }
+          for (int i = 0; i < 8; i++) mx = max_u16x2(mx, pk[i]);
         }
+        T::put(smem, c, fm, fn, pk);
       }
     }
+    mx = (mx >> 16) > (mx & 0xffffu) ? (mx >> 16) : (mx & 0xffffu);
     mx = wave_max_u32(mx);
-    uint32_t* red = (uint32_t*)smem;
-    __syncthreads();  // other waves may still read the last pipeline stage
+    uint32_t* red = (uint32_t*)(smem + T::BYTES);
     if (c.lane == 0) red[threadIdx.x >> 6] = mx;
     __syncthreads();
+    T::rows(smem, c, [&](int64_t m, int64_t n, uint4 v) {
+      *(uint4*)(post + m * ld + n) = v;
+      if (post_q) {
+        uint2 q;
+        q.x = pack_e4m3x4_nonneg(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
+        q.y = pack_e4m3x4_nonneg(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
+        *(uint2*)(post_q + m * ld + n) = q;
+      }
+    });
     if (threadIdx.x == 0) {
       uint32_t m4 = red[0];
       for (int i = 1; i < 4; i++) m4 = red[i] > m4 ? red[i] : m4;
-      partial[c.tm * tiles_n + c.tn] = __uint_as_float(m4);
+      partial[c.tm * tiles_n + c.tn] = __uint_as_float(m4 << 16);
     }
   }
 };
@@ -92,7 +156,11 @@ struct EpiBf16Out {
   const float* w_inv;
 
   template <class C>
-  __device__ __forceinline__ void run(const TileCtx& c, f32x16 (&acc)[C::FM][C::FN], FP8MLP_LDS char*) {
+  static constexpr int lds_bytes() { return Tile16<C>::BYTES; }
+
+  template <class C>
+  __device__ __forceinline__ void run(const TileCtx& c, f32x16 (&acc)[C::FM][C::FN], FP8MLP_LDS char* smem) {
+    using T = Tile16<C>;
     float inv_s = 1.0f, inv_w = 1.0f;
     if (mode == 1) {
       inv_s = 1.0f / scale_from_amax(*amax_prev, margin);
@@ -101,60 +169,57 @@ struct EpiBf16Out {
       inv_s = 1.0f / *x_scale;
       inv_w = *w_inv;
     }
+    __syncthreads();
 #pragma unroll
     for (int fm = 0; fm < C::FM; fm++) {
-      const int64_t m = c.m0 + epi_row<C>(c, fm);
-      if (m >= c.M) continue;
 #pragma unroll
       for (int fn = 0; fn < C::FN; fn++) {
         float v[16];
 #pragma unroll
         for (int e = 0; e < 16; e++) v[e] = mode ? (acc[fm][fn][e] * inv_s) * inv_w : acc[fm][fn][e];
-        if constexpr (C::PERM) {
-          const int64_t n = c.n0 + epi_col<C>(c, fn, 0);
-          if (n < c.N) {
-            uint16_t* dst = y + m * ld + n;
-            *(uint4*)dst = uint4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                                 pack_bf16x2(v[6], v[7])};
-            *(uint4*)(dst + 8) = uint4{pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]),
-                                       pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15])};
-          }
-        } else {
+        uint32_t w[8];
 #pragma unroll
-          for (int g = 0; g < 4; g++) {
-            const int64_t n = c.n0 + epi_col<C>(c, fn, 4 * g);
-            if (n < c.N)
-              *(uint2*)(y + m * ld + n) =
-                  uint2{pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3])};
-          }
-        }
+        for (int i = 0; i < 8; i++) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+        T::put(smem, c, fm, fn, w);
       }
     }
+    __syncthreads();
+    T::rows(smem, c, [&](int64_t m, int64_t n, uint4 v) { *(uint4*)(y + m * ld + n) = v; });
   }
 };
 
 // Backward dgrad epilogue ("NanoGPT Speedrun (Track 1)", "Changes vs Record
 // #83" item 4: relu(pre) is rebuilt from the stored post as sqrt(post)):
 //   dpre = bf16(2 * sqrt(post) * dpost),  dpost = the accumulator
+// The post tile is brought into LDS in row order, combined there with the
+// accumulators in place, and dpre leaves in row order.
 struct EpiDpre {
   const uint16_t* post;
   uint16_t* dpre;
   int64_t ld;  // h
 
   template <class C>
-  __device__ __forceinline__ void run(const TileCtx& c, f32x16 (&acc)[C::FM][C::FN], FP8MLP_LDS char*) {
+  static constexpr int lds_bytes() { return Tile16<C>::BYTES; }
+
+  template <class C>
+  __device__ __forceinline__ void run(const TileCtx& c, f32x16 (&acc)[C::FM][C::FN], FP8MLP_LDS char* smem) {
     static_assert(C::PERM, "needs 16 consecutive columns per lane");
+    using T = Tile16<C>;
+    __syncthreads();
+    T::load(smem, c, post, ld);
+    wait_vmcnt<0>();
+    __syncthreads();
 #pragma unroll
     for (int fm = 0; fm < C::FM; fm++) {
-      const int64_t m = c.m0 + epi_row<C>(c, fm);
-      if (m >= c.M) continue;
+      const int row = T::frag_row(c, fm);
 #pragma unroll
       for (int fn = 0; fn < C::FN; fn++) {
-        const int64_t n = c.n0 + epi_col<C>(c, fn, 0);
-        if (n >= c.N) continue;
-        const uint16_t* src = post + m * ld + n;
-        const uint4 p0 = *(const uint4*)src, p1 = *(const uint4*)(src + 8);
-        const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        const int ch = T::frag_chunk(c, fn);
+        FP8MLP_LDS i32x4* p0 = (FP8MLP_LDS i32x4*)(smem + T::off(row, ch));
+        FP8MLP_LDS i32x4* p1 = (FP8MLP_LDS i32x4*)(smem + T::off(row, ch + 1));
+        const i32x4 a = *p0, b = *p1;
+        const uint32_t pw[8] = {(uint32_t)a[0], (uint32_t)a[1], (uint32_t)a[2], (uint32_t)a[3],
+                                (uint32_t)b[0], (uint32_t)b[1], (uint32_t)b[2], (uint32_t)b[3]};
         uint32_t o[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
@@ -162,11 +227,12 @@ struct EpiDpre {
           const float r0 = __builtin_amdgcn_sqrtf(bf16_lo(pw[i])), r1 = __builtin_amdgcn_sqrtf(bf16_hi(pw[i]));
           o[i] = pack_bf16x2((2.0f * r0) * acc[fm][fn][2 * i], (2.0f * r1) * acc[fm][fn][2 * i + 1]);
         }
-        uint16_t* dst = dpre + m * ld + n;
-        *(uint4*)dst = uint4{o[0], o[1], o[2], o[3]};
-        *(uint4*)(dst + 8) = uint4{o[4], o[5], o[6], o[7]};
+        *p0 = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+        *p1 = i32x4{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
       }
     }
+    __syncthreads();
+    T::rows(smem, c, [&](int64_t m, int64_t n, uint4 v) { *(uint4*)(dpre + m * ld + n) = v; });
   }
 };
 
@@ -177,6 +243,9 @@ struct EpiF32 {
   int64_t ld;
   int64_t split_stride;   // elements between split partials (0: single split)
   int accumulate;         // add into out (single split only)
+
+  template <class C>
+  static constexpr int lds_bytes() { return 0; }
 
   template <class C>
   __device__ __forceinline__ void run(const TileCtx& c, f32x16 (&acc)[C::FM][C::FN], FP8MLP_LDS char*) {

@@ -178,7 +178,11 @@ __device__ __forceinline__ uint32_t load_off(int c, int64_t ld_bytes) {
 // ------------------------------------------------------------------ kernel
 template <class C, class Epi>
 __global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS_BYTES];
+  // the pipeline buffers, reused by the epilogue once the last tile is read
+  constexpr int EPI_BYTES = Epi::template lds_bytes<C>();
+  constexpr int SMEM = C::LDS_BYTES > EPI_BYTES ? C::LDS_BYTES : EPI_BYTES;
+  static_assert(SMEM * C::OCC <= 160 * 1024, "LDS with the epilogue's staging");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[SMEM];
   FP8MLP_LDS char* smem = (FP8MLP_LDS char*)smem_raw;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
