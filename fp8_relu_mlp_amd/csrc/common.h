@@ -113,12 +113,32 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, FP8M
                                                   uint32_t voffset) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, voffset, 0, 0, 0);
 }
+// The same with the non-temporal (streaming) cache policy, for data read once.
+__device__ __forceinline__ void buffer_load_lds16_stream(__amdgpu_buffer_rsrc_t r, FP8MLP_LDS void* lds_wave_base,
+                                                         uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, voffset, 0, 0, 2 /* nt */);
+}
+// Non-temporal stores of 16 and 8 bytes (written once, not re-read soon).
+__device__ __forceinline__ void store_stream(void* p, uint4 v) {
+  __builtin_nontemporal_store(i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, (i32x4*)p);
+}
+__device__ __forceinline__ void store_stream(void* p, uint2 v) {
+  __builtin_nontemporal_store(i32x2{(int)v.x, (int)v.y}, (i32x2*)p);
+}
+
 // s_waitcnt vmcnt(n) with the other counters left unconstrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
+
+// Block barrier for the GEMM main loops: this wave's LDS operations are
+// complete, then s_barrier.  Unlike __syncthreads() it does not wait for
+// outstanding global loads, including loads that write LDS directly, whose
+// completion the loops wait for explicitly (and only where needed).  The
+// "memory" clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ i32x4 lds_read_b128(const FP8MLP_LDS char* base, uint32_t off) {
   return *(const FP8MLP_LDS i32x4*)(base + off);

@@ -9,7 +9,9 @@ namespace fp8mlp {
 // ------------------------------------------------------------------ LDS staging
 // In the accumulator layout one store instruction of a wave touches 32 rows;
 // 16-bit results therefore go through LDS and leave row by row: 16 bytes per
-// lane, 8 lanes per 128-byte line.  LDS image of the BM x BN tile: rows of
+// lane, 8 lanes per 128-byte line.  The activation-sized outputs are written
+// with the streaming (non-temporal) hint so they do not push the GEMM
+// operands out of L2.  LDS image of the BM x BN tile: rows of
 // BN/8 chunks of 16 bytes, the chunk index XOR-ed with the row's low bits, so
 // the fragment-order writes (16 lanes = 16 consecutive rows, one chunk) and
 // the row-order reads (16 lanes = 16 chunks of one row) both use 16 distinct
@@ -19,8 +21,8 @@ struct Tile16 {
   static constexpr int CPR = C::BN / 8;                    // 16-byte chunks per row
   static constexpr int XM = CPR < 16 ? CPR - 1 : 15;
   static constexpr int BYTES = C::BM * C::BN * 2;
-  static constexpr int PASSES = C::BM * CPR / 256;         // row-order passes of the block
-  static_assert((C::BM * CPR) % 256 == 0, "row-order passes");
+  static constexpr int PASSES = C::BM * CPR / C::NT;      // row-order passes of the block
+  static_assert((C::BM * CPR) % C::NT == 0, "row-order passes");
   __device__ static __forceinline__ uint32_t off(int row, int chunk) {
     return (uint32_t)(row * CPR + (chunk ^ (row & XM))) * 16u;
   }
@@ -47,7 +49,7 @@ struct Tile16 {
   __device__ static __forceinline__ void rows(const FP8MLP_LDS char* s, const TileCtx& c, F&& f) {
 #pragma unroll
     for (int p = 0; p < PASSES; p++) {
-      const int i = p * 256 + (int)threadIdx.x;
+      const int i = p * C::NT + (int)threadIdx.x;
       const int row = i / CPR, ch = i % CPR;
       const i32x4 r = lds_read_b128(s, off(row, ch));
       const uint4 v{(uint32_t)r[0], (uint32_t)r[1], (uint32_t)r[2], (uint32_t)r[3]};
@@ -56,16 +58,17 @@ struct Tile16 {
     }
   }
   // Global 16-bit matrix (leading dimension ld) -> LDS image, loaded straight
-  // into LDS in row order; rows past the matrix end read as zero.
+  // into LDS in row order (streaming: read once); rows past the matrix end
+  // read as zero.
   __device__ static __forceinline__ void load(FP8MLP_LDS char* s, const TileCtx& c, const uint16_t* g, int64_t ld) {
     const uint16_t* base = g + c.m0 * ld + c.n0;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (uint64_t)((c.M - c.m0) * ld - c.n0) * 2u);
     const int wave = threadIdx.x >> 6;
 #pragma unroll
     for (int p = 0; p < PASSES; p++) {
-      const int i = (p * 4 + wave) * 64 + c.lane;   // LDS-linear chunk this lane fills
+      const int i = (p * C::NW + wave) * 64 + c.lane;   // LDS-linear chunk this lane fills
       const int row = i / CPR, ch = (i % CPR) ^ (row & XM);
-      buffer_load_lds16(r, s + (p * 4 + wave) * 1024, (uint32_t)(row * ld * 2 + ch * 16));
+      buffer_load_lds16_stream(r, s + (p * C::NW + wave) * 1024, (uint32_t)(row * ld * 2 + ch * 16));
     }
   }
 };
@@ -96,7 +99,7 @@ struct EpiRelu2Quant {
   int tiles_n;
 
   template <class C>
-  static constexpr int lds_bytes() { return Tile16<C>::BYTES + 16; }
+  static constexpr int lds_bytes() { return Tile16<C>::BYTES + 4 * C::NW; }
 
   template <class C>
   __device__ __forceinline__ void run(const TileCtx& c, f32x16 (&acc)[C::FM][C::FN], FP8MLP_LDS char* smem) {
@@ -126,17 +129,17 @@ struct EpiRelu2Quant {
     if (c.lane == 0) red[threadIdx.x >> 6] = mx;
     __syncthreads();
     T::rows(smem, c, [&](int64_t m, int64_t n, uint4 v) {
-      *(uint4*)(post + m * ld + n) = v;
+      store_stream(post + m * ld + n, v);
       if (post_q) {
         uint2 q;
         q.x = pack_e4m3x4_nonneg(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
         q.y = pack_e4m3x4_nonneg(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
-        *(uint2*)(post_q + m * ld + n) = q;
+        store_stream(post_q + m * ld + n, q);
       }
     });
     if (threadIdx.x == 0) {
       uint32_t m4 = red[0];
-      for (int i = 1; i < 4; i++) m4 = red[i] > m4 ? red[i] : m4;
+      for (int i = 1; i < C::NW; i++) m4 = red[i] > m4 ? red[i] : m4;
       partial[c.tm * tiles_n + c.tn] = __uint_as_float(m4 << 16);
     }
   }
@@ -184,7 +187,7 @@ struct EpiBf16Out {
       }
     }
     __syncthreads();
-    T::rows(smem, c, [&](int64_t m, int64_t n, uint4 v) { *(uint4*)(y + m * ld + n) = v; });
+    T::rows(smem, c, [&](int64_t m, int64_t n, uint4 v) { store_stream(y + m * ld + n, v); });
   }
 };
 
@@ -232,7 +235,7 @@ struct EpiDpre {
       }
     }
     __syncthreads();
-    T::rows(smem, c, [&](int64_t m, int64_t n, uint4 v) { *(uint4*)(dpre + m * ld + n) = v; });
+    T::rows(smem, c, [&](int64_t m, int64_t n, uint4 v) { store_stream(dpre + m * ld + n, v); });
   }
 };
 

@@ -35,7 +35,7 @@ namespace fp8mlp {
 
 enum { KC = 0, MNC = 1 };
 
-template <int ELT_, int BM_, int BN_, int RB_, int STAGES_, int OCC_, int QL_, int PL_, int REG_ = 0>
+template <int ELT_, int BM_, int BN_, int RB_, int STAGES_, int OCC_, int QL_, int PL_, int REG_ = 0, int NW_ = 4>
 struct GemmCfg {
   static constexpr int ELT = ELT_;                 // bytes per element: 2 bf16, 1 e4m3
   // REG == 1: tiles go global -> VGPRs -> LDS (buffer_load_dwordx4 +
@@ -49,22 +49,31 @@ struct GemmCfg {
   static constexpr int BK = RB / ELT;              // k per tile
   static constexpr int STAGES = STAGES_, OCC = OCC_;
   static constexpr int QL = QL_, PL = PL_;
-  static constexpr int WTM = BM / 2, WTN = BN / 2; // wave tile
+  // NW == 4: one 256-thread block, 2 x 2 waves, every wave loads and
+  // computes.  NW == 8: 512 threads, 2 x 4 waves in two groups of four (one
+  // wave of each group per SIMD) that take turns: while one group issues its
+  // MFMAs the other reads its next fragments and issues the global loads
+  // (gemm_pp_kernel).
+  static constexpr int NW = NW_, NT = 64 * NW_;
+  static constexpr int WTM = BM / 2, WTN = BN / (NW_ / 2); // wave tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int KSTEP = ELT == 2 ? 32 : 64; // bytes of k per MFMA
   static constexpr int SL = RB / KSTEP;            // MFMA k-steps per tile
   static constexpr int Q_BYTES = BM * RB, P_BYTES = BN * RB;
   static constexpr int STAGE_BYTES = Q_BYTES + P_BYTES;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-  static constexpr int Q_LOADS = Q_BYTES / 4096;   // 16 B x 64 lanes x 4 waves per round
-  static constexpr int P_LOADS = P_BYTES / 4096;
+  static constexpr int Q_LOADS = Q_BYTES / (1024 * NW);   // 16 B x 64 lanes x NW waves per round
+  static constexpr int P_LOADS = P_BYTES / (1024 * NW);
   static constexpr int LOADS = Q_LOADS + P_LOADS;
   // the P operand's row order gives each lane 16 consecutive n, except for
   // transposed fp8 reads, which give 4 runs of 4
   static constexpr bool PERM = !(ELT == 1 && PL == MNC);
   static_assert(RB == 64 || RB == 128, "row bytes");
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
-  static_assert(Q_BYTES % 4096 == 0 && P_BYTES % 4096 == 0, "loads");
+  static_assert(NW == 4 || NW == 8, "waves");
+  static_assert(WTN % 32 == 0 && WTM % 32 == 0, "wave tile");
+  static_assert(Q_BYTES % (1024 * NW) == 0 && P_BYTES % (1024 * NW) == 0, "loads");
+  static_assert(NW == 4 || (REG == 0 && STAGES == 2 && OCC == 1), "the two-group kernel: direct loads, two buffers");
   // the row-contiguous swizzle XORs bits 6-7 (bf16) or 4-6 (e4m3) of the byte offset
   static_assert(QL == KC || (BM * ELT) % (ELT == 2 ? 256 : 128) == 0, "row-contiguous Q tile rows");
   static_assert(PL == KC || (BN * ELT) % (ELT == 2 ? 256 : 128) == 0, "row-contiguous P tile rows");
@@ -159,6 +168,51 @@ __device__ __forceinline__ void sched_tile() {
   }(std::make_integer_sequence<int, SL>{});
 }
 
+// Scheduling groups for one k-slice of NM MFMAs.  After MFMA i comes its
+// share of the other instructions of the slice:
+//  * NR LDS reads (fragments of the next slice), over the first half of the
+//    MFMAs when there are LDS writes, else over all of them, front-loaded;
+//  * NW LDS writes (register staging) over the third quarter and then the NV
+//    global loads that refill those registers over the last quarter (in the
+//    program order the reads, the writes and the loads come in that order,
+//    and the writes may alias the reads);
+//  * without LDS writes, the NV global loads (direct to LDS, which may alias
+//    the reads as far as the compiler knows) over the second half.
+template <int N, int LEN, int I>
+constexpr int share_front() { return (N * (I + 1) + LEN - 1) / LEN - (N * I + LEN - 1) / LEN; }
+template <int NM, int NR, int NW, int NV, int I = 0>
+__device__ __forceinline__ void sched_mix() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (NW > 0) {
+      constexpr int H = NM / 2, Q3 = (3 * NM) / 4;
+      if constexpr (I < H) {
+        constexpr int r = share_front<NR, H, I>();
+        if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+      } else if constexpr (I < Q3) {
+        constexpr int w = share_front<NW, Q3 - H, I - H>();
+        if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(0x200, w, 0);
+      } else {
+        constexpr int v = share_front<NV, NM - Q3, I - Q3>();
+        if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
+      }
+    } else if constexpr (NV > 0) {
+      constexpr int H = NM / 2;
+      if constexpr (I < H) {
+        constexpr int r = share_front<NR, H, I>();
+        if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+      } else {
+        constexpr int v = share_front<NV, NM - H, I - H>();
+        if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
+      }
+    } else {
+      constexpr int r = share_front<NR, NM, I>();
+      if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+    }
+    sched_mix<NM, NR, NW, NV, I + 1>();
+  }
+}
+
 // LDS-linear 16-byte chunk c of an operand tile -> byte offset in global
 // memory relative to the tile origin (at k = 0 of this block's range).
 template <class C, int L, int ROWS, bool IS_P>
@@ -175,158 +229,130 @@ __device__ __forceinline__ uint32_t load_off(int c, int64_t ld_bytes) {
   }
 }
 
-// ------------------------------------------------------------------ kernel
-template <class C, class Epi>
-__global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) {
-  // the pipeline buffers, reused by the epilogue once the last tile is read
-  constexpr int EPI_BYTES = Epi::template lds_bytes<C>();
-  constexpr int SMEM = C::LDS_BYTES > EPI_BYTES ? C::LDS_BYTES : EPI_BYTES;
-  static_assert(SMEM * C::OCC <= 160 * 1024, "LDS with the epilogue's staging");
-  __shared__ __attribute__((aligned(1024))) char smem_raw[SMEM];
-  FP8MLP_LDS char* smem = (FP8MLP_LDS char*)smem_raw;
-
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int h = lane >> 5;
-
-  // With two blocks per CU, blocks that start together reach their
-  // epilogues together and leave the matrix cores idle meanwhile.  Delaying
-  // the blocks that the dispatcher places in the second residency slot of
-  // each CU (the second 256 of the first 512) shifts the two slots by part of
-  // a tile; later blocks inherit the offset when they take over a slot.
-  if (C::OCC > 1 && a.stagger > 0 && blockIdx.x >= 256 && blockIdx.x < 512) {
-    for (int i = 0; i < a.stagger; i++) __builtin_amdgcn_s_sleep(127);
-  }
-
-  // ---- tile assignment.  Consecutive blocks go round-robin over the 8 XCDs;
-  // xcd_remap gives each XCD a contiguous run of logical tiles.  Logical
-  // order: split-k index slowest (blocks of one split share their k-range of
-  // both operands), then groups of GROUP_M tile rows, inside a group the row
-  // fastest, so the tiles an XCD runs at once form a near-square window that
-  // shares few A- and B-slabs in that XCD's L2.
+// ------------------------------------------------------------------ shared kernel pieces
+// Tile assignment.  Consecutive blocks go round-robin over the 8 XCDs;
+// xcd_remap gives each XCD a contiguous run of logical tiles.  Logical order:
+// split-k index slowest (blocks of one split share their k-range of both
+// operands), then groups of group_m tile rows, inside a group the row fastest,
+// so the tiles an XCD runs at once form a near-square window that shares few
+// A- and B-slabs in that XCD's L2.
+struct TilePos {
+  int tm, tn, split, KT;
+  int64_t m0, n0, kb, ke;
+};
+template <class C>
+__device__ __forceinline__ TilePos tile_pos(const GemmArgs& a) {
+  TilePos t;
   const int GROUP_M = a.group_m;
-  int t = xcd_remap(blockIdx.x, gridDim.x);
+  int i = xcd_remap(blockIdx.x, gridDim.x);
   const int per_split = a.tiles_m * a.tiles_n;
-  const int split = t / per_split;
-  t -= split * per_split;
+  t.split = i / per_split;
+  i -= t.split * per_split;
   const int per_group = GROUP_M * a.tiles_n;
-  const int grp = t / per_group, rem = t - grp * per_group;
+  const int grp = i / per_group, rem = i - grp * per_group;
   const int gm = min(GROUP_M, a.tiles_m - grp * GROUP_M);
-  const int tm = grp * GROUP_M + rem % gm, tn = rem / gm;
-  const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
-  const int64_t kb = (int64_t)split * a.k_per_split;
-  const int64_t ke = min(a.K, kb + a.k_per_split);
-  const int KT = (int)((ke - kb + C::BK - 1) / C::BK);
+  t.tm = grp * GROUP_M + rem % gm;
+  t.tn = rem / gm;
+  t.m0 = (int64_t)t.tm * C::BM;
+  t.n0 = (int64_t)t.tn * C::BN;
+  t.kb = (int64_t)t.split * a.k_per_split;
+  t.ke = min(a.K, t.kb + a.k_per_split);
+  t.KT = (int)((t.ke - t.kb + C::BK - 1) / C::BK);
+  return t;
+}
 
-  // ---- buffer resources anchored at the tile origin
-  const int64_t ldq_b = a.ldq * C::ELT, ldp_b = a.ldp * C::ELT;
+// Global -> LDS loads of the two operand tiles: buffer resources anchored at
+// the tile origin (rows k >= ke of a row-contiguous operand fall past the
+// resource's end and load as zero; for k-contiguous operands K is a multiple
+// of BK) and this lane's byte offsets for each of its 16-byte chunks.
+template <class C>
+struct TileLoads {
   __amdgpu_buffer_rsrc_t rq, rp;
-  {
+  uint32_t qoff[C::Q_LOADS], poff[C::P_LOADS];
+  uint32_t qstep, pstep;   // bytes between consecutive k-tiles
+
+  __device__ __forceinline__ void init(const GemmArgs& a, const TilePos& t, int wave, int lane) {
+    const int64_t ldq_b = a.ldq * C::ELT, ldp_b = a.ldp * C::ELT;
     const char* q = (const char*)a.q;
     const char* p = (const char*)a.p;
     if constexpr (C::QL == KC) {
-      rq = make_rsrc(q + m0 * ldq_b + kb * C::ELT, (uint64_t)((a.M - m0) * ldq_b - kb * C::ELT));
+      rq = make_rsrc(q + t.m0 * ldq_b + t.kb * C::ELT, (uint64_t)((a.M - t.m0) * ldq_b - t.kb * C::ELT));
     } else {
-      rq = make_rsrc(q + kb * ldq_b + m0 * C::ELT, (uint64_t)((ke - kb) * ldq_b - m0 * C::ELT));
+      rq = make_rsrc(q + t.kb * ldq_b + t.m0 * C::ELT, (uint64_t)((t.ke - t.kb) * ldq_b - t.m0 * C::ELT));
     }
     if constexpr (C::PL == KC) {
-      rp = make_rsrc(p + n0 * ldp_b + kb * C::ELT, (uint64_t)((a.N - n0) * ldp_b - kb * C::ELT));
+      rp = make_rsrc(p + t.n0 * ldp_b + t.kb * C::ELT, (uint64_t)((a.N - t.n0) * ldp_b - t.kb * C::ELT));
     } else {
-      rp = make_rsrc(p + kb * ldp_b + n0 * C::ELT, (uint64_t)((ke - kb) * ldp_b - n0 * C::ELT));
+      rp = make_rsrc(p + t.kb * ldp_b + t.n0 * C::ELT, (uint64_t)((t.ke - t.kb) * ldp_b - t.n0 * C::ELT));
     }
+#pragma unroll
+    for (int j = 0; j < C::Q_LOADS; j++)
+      qoff[j] = load_off<C, C::QL, C::BM, false>((j * C::NW + wave) * 64 + lane, ldq_b);
+#pragma unroll
+    for (int j = 0; j < C::P_LOADS; j++)
+      poff[j] = load_off<C, C::PL, C::BN, true>((j * C::NW + wave) * 64 + lane, ldp_b);
+    qstep = C::QL == KC ? (uint32_t)C::RB : (uint32_t)(C::BK * ldq_b);
+    pstep = C::PL == KC ? (uint32_t)C::RB : (uint32_t)(C::BK * ldp_b);
   }
-  // Rows k >= ke of a row-contiguous operand fall past the resource's end and
-  // load as zero; for k-contiguous operands K is a multiple of BK.
-
-  uint32_t qoff[C::Q_LOADS], poff[C::P_LOADS];
-#pragma unroll
-  for (int j = 0; j < C::Q_LOADS; j++) qoff[j] = load_off<C, C::QL, C::BM, false>((j * 4 + wave) * 64 + lane, ldq_b);
-#pragma unroll
-  for (int j = 0; j < C::P_LOADS; j++) poff[j] = load_off<C, C::PL, C::BN, true>((j * 4 + wave) * 64 + lane, ldp_b);
-  const uint32_t qstep = C::QL == KC ? (uint32_t)C::RB : (uint32_t)(C::BK * ldq_b);
-  const uint32_t pstep = C::PL == KC ? (uint32_t)C::RB : (uint32_t)(C::BK * ldp_b);
-
-  // register staging: the next tile in flight in VGPRs
-  i32x4 rq_regs[1][C::REG ? C::Q_LOADS : 1], rp_regs[1][C::REG ? C::P_LOADS : 1];
-  auto gload = [&](int kt, int slot) {
-    const uint32_t dq = (uint32_t)kt * qstep, dp = (uint32_t)kt * pstep;
-#pragma unroll
-    for (int j = 0; j < C::Q_LOADS; j++)
-      rq_regs[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff[j] + dq, 0, 0);
-#pragma unroll
-    for (int j = 0; j < C::P_LOADS; j++)
-      rp_regs[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(rp, poff[j] + dp, 0, 0);
-  };
-  auto dswrite = [&](int stage, int slot) {
-    FP8MLP_LDS char* sq = smem + stage * C::STAGE_BYTES;
-    FP8MLP_LDS char* sp = sq + C::Q_BYTES;
-#pragma unroll
-    for (int j = 0; j < C::Q_LOADS; j++)
-      *(FP8MLP_LDS i32x4*)(sq + ((j * 4 + wave) * 64 + lane) * 16) = rq_regs[slot][j];
-#pragma unroll
-    for (int j = 0; j < C::P_LOADS; j++)
-      *(FP8MLP_LDS i32x4*)(sp + ((j * 4 + wave) * 64 + lane) * 16) = rp_regs[slot][j];
-  };
-
-  auto issue = [&](int kt, int stage) {
+  // this wave's share of k-tile kt, straight into LDS stage `stage`
+  __device__ __forceinline__ void issue(FP8MLP_LDS char* smem, int kt, int stage, int wave) const {
     FP8MLP_LDS char* sq = smem + stage * C::STAGE_BYTES;
     FP8MLP_LDS char* sp = sq + C::Q_BYTES;
     const uint32_t dq = (uint32_t)kt * qstep, dp = (uint32_t)kt * pstep;
 #pragma unroll
-    for (int j = 0; j < C::Q_LOADS; j++) buffer_load_lds16(rq, sq + (j * 4 + wave) * 1024, qoff[j] + dq);
+    for (int j = 0; j < C::Q_LOADS; j++) buffer_load_lds16(rq, sq + (j * C::NW + wave) * 1024, qoff[j] + dq);
 #pragma unroll
-    for (int j = 0; j < C::P_LOADS; j++) buffer_load_lds16(rp, sp + (j * 4 + wave) * 1024, poff[j] + dp);
-  };
+    for (int j = 0; j < C::P_LOADS; j++) buffer_load_lds16(rp, sp + (j * C::NW + wave) * 1024, poff[j] + dp);
+  }
+};
 
-  // ---- fragment read offsets (bytes within a stage's Q / P tile)
-  // Q: MFMA column q = lane & 31  -> tile row wm*WTM + fm*32 + (lane & 31)
-  // P: MFMA row p' = lane & 31   -> tile row wn*WTN + fn*32 + perm_p(p') (or p')
+// MFMA operand fragments read from one LDS stage.
+//   Q: MFMA column q = lane & 31  -> tile row wm*WTM + fm*32 + (lane & 31)
+//   P: MFMA row p' = lane & 31   -> tile row wn*WTN + fn*32 + perm_p(p') (or p')
+template <class C>
+struct FragReader {
+  using Frag = typename FragT<C::ELT>::type;
+  int lane, h;
   int qrow_off, prow_off;   // per-lane part; fragments add fm*32 / fn*32 rows
   int qx, px;               // swizzle terms
-  if constexpr (C::QL == KC) {
-    const int r = wm * C::WTM + (lane & 31);
-    qrow_off = r * C::RB;
-    qx = swz_rows_q<C::CPR>(r);
-  } else {
-    // transposed read: source lanes supply k = .. + ((lane & 15) >> 2) and
-    // 4 consecutive rows starting at mb
-    const int kq = (lane & 15) >> 2;
-    const int mb = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    qrow_off = (8 * h + kq) * (C::BM * 2);
-    qx = 2 * (wm * C::WTM + mb);
+
+  __device__ __forceinline__ void init(int wm, int wn, int lane_) {
+    lane = lane_;
+    h = lane >> 5;
+    if constexpr (C::QL == KC) {
+      const int r = wm * C::WTM + (lane & 31);
+      qrow_off = r * C::RB;
+      qx = swz_rows_q<C::CPR>(r);
+    } else {
+      // transposed read: source lanes supply k = .. + ((lane & 15) >> 2) and
+      // 4 consecutive rows starting at mb
+      const int kq = (lane & 15) >> 2;
+      const int mb = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      qrow_off = (8 * h + kq) * (C::BM * 2);
+      qx = 2 * (wm * C::WTM + mb);
+    }
+    if constexpr (C::PL == KC) {
+      const int r = wn * C::WTN + (C::PERM ? perm_p(lane & 31) : (lane & 31));
+      prow_off = r * C::RB;
+      px = swz_rows_p<C::CPR>(r);
+    } else if constexpr (C::ELT == 2) {
+      const int kq = (lane & 15) >> 2;
+      const int q4 = lane & 3;
+      const int mb = 16 * (q4 & 1) + 8 * ((lane >> 4) & 1) + 4 * (q4 >> 1);
+      prow_off = (8 * h + kq) * (C::BN * 2);
+      px = 2 * (wn * C::WTN + mb);
+    } else {
+      const int kq = (lane & 15) >> 1;
+      const int nb = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+      prow_off = (32 * h + kq) * C::BN;
+      px = wn * C::WTN + nb;
+    }
   }
-  if constexpr (C::PL == KC) {
-    const int r = wn * C::WTN + (C::PERM ? perm_p(lane & 31) : (lane & 31));
-    prow_off = r * C::RB;
-    px = swz_rows_p<C::CPR>(r);
-  } else if constexpr (C::ELT == 2) {
-    const int kq = (lane & 15) >> 2;
-    const int q4 = lane & 3;
-    const int mb = 16 * (q4 & 1) + 8 * ((lane >> 4) & 1) + 4 * (q4 >> 1);
-    prow_off = (8 * h + kq) * (C::BN * 2);
-    px = 2 * (wn * C::WTN + mb);
-  } else {
-    const int kq = (lane & 15) >> 1;
-    const int nb = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-    prow_off = (32 * h + kq) * C::BN;
-    px = wn * C::WTN + nb;
-  }
+  // LDS reads per fragment
+  static constexpr int QR = C::QL == KC ? (C::ELT == 2 ? 1 : 2) : (C::ELT == 2 ? 2 : 4);
+  static constexpr int PR = C::PL == KC ? (C::ELT == 2 ? 1 : 2) : (C::ELT == 2 ? 2 : 4);
 
-  f32x16 acc[C::FM][C::FN];
-#pragma unroll
-  for (int i = 0; i < C::FM; i++)
-#pragma unroll
-    for (int j = 0; j < C::FN; j++)
-#pragma unroll
-      for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
-
-  // ---- fragment loaders and the MFMA
-  using Frag = typename FragT<C::ELT>::type;
-  constexpr int QR = C::QL == KC ? (C::ELT == 2 ? 1 : 2) : (C::ELT == 2 ? 2 : 4);  // LDS reads per fragment
-  constexpr int PR = C::PL == KC ? (C::ELT == 2 ? 1 : 2) : (C::ELT == 2 ? 2 : 4);
-  constexpr int NREADS = C::FM * QR + C::FN * PR;
-
-  auto load_q = [&](const FP8MLP_LDS char* sq, int s, int fm) -> Frag {
+  __device__ __forceinline__ Frag q(const FP8MLP_LDS char* sq, int s, int fm) const {
     if constexpr (C::ELT == 2) {
       if constexpr (C::QL == KC) {
         const uint32_t off = qrow_off + fm * 32 * C::RB + (((2 * s + h) ^ qx) * 16);
@@ -343,8 +369,8 @@ __global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) 
       const i32x4 v1 = lds_read_b128(sq, base + (((4 * s + 2 * h + 1) ^ qx) * 16));
       return i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     }
-  };
-  auto load_p = [&](const FP8MLP_LDS char* sp, int s, int fn) -> Frag {
+  }
+  __device__ __forceinline__ Frag p(const FP8MLP_LDS char* sp, int s, int fn) const {
     if constexpr (C::ELT == 2) {
       if constexpr (C::PL == KC) {
         const uint32_t off = prow_off + fn * 32 * C::RB + (((2 * s + h) ^ px) * 16);
@@ -372,80 +398,279 @@ __global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) 
         return i32x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
       }
     }
+  }
+};
+
+template <class C>
+__device__ __forceinline__ f32x16 mma(const typename FragT<C::ELT>::type& p, const typename FragT<C::ELT>::type& q,
+                                      const f32x16& c) {
+  if constexpr (C::ELT == 2) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(p, q, c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(p, q, c, 0, 0, 0, 127, 0, 127);
+  }
+}
+
+// ------------------------------------------------------------------ kernel: 4 waves
+template <class C, class Epi>
+__global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) {
+  static_assert(C::NW == 4, "four-wave kernel");
+  // the pipeline buffers, reused by the epilogue once the last tile is read
+  constexpr int EPI_BYTES = Epi::template lds_bytes<C>();
+  constexpr int SMEM = C::LDS_BYTES > EPI_BYTES ? C::LDS_BYTES : EPI_BYTES;
+  static_assert(SMEM * C::OCC <= 160 * 1024, "LDS with the epilogue's staging");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[SMEM];
+  FP8MLP_LDS char* smem = (FP8MLP_LDS char*)smem_raw;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // With two blocks per CU, blocks that start together reach their
+  // epilogues together and leave the matrix cores idle meanwhile.  Delaying
+  // the blocks that the dispatcher places in the second residency slot of
+  // each CU (the second 256 of the first 512) shifts the two slots by part of
+  // a tile; later blocks inherit the offset when they take over a slot.
+  if (C::OCC > 1 && a.stagger > 0 && blockIdx.x >= 256 && blockIdx.x < 512) {
+    for (int i = 0; i < a.stagger; i++) __builtin_amdgcn_s_sleep(127);
+  }
+
+  const TilePos t = tile_pos<C>(a);
+  const int KT = t.KT;
+  TileLoads<C> ld;
+  ld.init(a, t, wave, lane);
+
+  // register staging: the next tile in flight in VGPRs
+  i32x4 rq_regs[C::REG ? C::Q_LOADS : 1], rp_regs[C::REG ? C::P_LOADS : 1];
+  auto gload = [&](int kt) {
+    const uint32_t dq = (uint32_t)kt * ld.qstep, dp = (uint32_t)kt * ld.pstep;
+#pragma unroll
+    for (int j = 0; j < C::Q_LOADS; j++) rq_regs[j] = __builtin_amdgcn_raw_buffer_load_b128(ld.rq, ld.qoff[j] + dq, 0, 0);
+#pragma unroll
+    for (int j = 0; j < C::P_LOADS; j++) rp_regs[j] = __builtin_amdgcn_raw_buffer_load_b128(ld.rp, ld.poff[j] + dp, 0, 0);
   };
-  auto mma = [](const Frag& p, const Frag& q, const f32x16& c) -> f32x16 {
-    if constexpr (C::ELT == 2) {
-      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(p, q, c, 0, 0, 0);
-    } else {
-      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(p, q, c, 0, 0, 0, 127, 0, 127);
-    }
+  auto dswrite = [&](int stage) {
+    FP8MLP_LDS char* sq = smem + stage * C::STAGE_BYTES;
+    FP8MLP_LDS char* sp = sq + C::Q_BYTES;
+#pragma unroll
+    for (int j = 0; j < C::Q_LOADS; j++) *(FP8MLP_LDS i32x4*)(sq + ((j * 4 + wave) * 64 + lane) * 16) = rq_regs[j];
+#pragma unroll
+    for (int j = 0; j < C::P_LOADS; j++) *(FP8MLP_LDS i32x4*)(sp + ((j * 4 + wave) * 64 + lane) * 16) = rp_regs[j];
   };
 
-  // ---- main loop: one barrier per tile
+  FragReader<C> fr;
+  fr.init(wm, wn, lane);
+  using Frag = typename FragT<C::ELT>::type;
+  constexpr int NREADS = C::FM * FragReader<C>::QR + C::FN * FragReader<C>::PR;
+
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; i++)
+#pragma unroll
+    for (int j = 0; j < C::FN; j++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
+
+  // ---- main loop.  One barrier per tile, placed just before the tile's last
+  // k-slice: by then every wave has read the slices it needs from this tile
+  // and the next tile is in LDS, so the reads of the next tile's first slice
+  // overlap the MFMAs of the last slice (fragments are double-buffered across
+  // slices and across tiles).  Global loads -- and, with register staging,
+  // the LDS writes -- are spread between the MFMAs of the earlier slices.
+  //   direct:   tile kt+STAGES-1 is issued in slice 0 of iteration kt, into
+  //             the buffer that held tile kt-1;
+  //   registers: in slice SL-2 of iteration kt, tile kt+1 goes from VGPRs to
+  //             LDS and tile kt+2 is loaded into the VGPRs.
+  static_assert(C::SL % 2 == 0, "fragment double-buffering across tiles needs an even slice count");
+  Frag qf[2][C::FM], pf[2][C::FN];
+  auto read_slice = [&](int stage, int s, Frag(&q)[C::FM], Frag(&p)[C::FN]) {
+    const FP8MLP_LDS char* sq = smem + stage * C::STAGE_BYTES;
+    const FP8MLP_LDS char* sp = sq + C::Q_BYTES;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; fm++) q[fm] = fr.q(sq, s, fm);
+#pragma unroll
+    for (int fn = 0; fn < C::FN; fn++) p[fn] = fr.p(sp, s, fn);
+  };
+
   if constexpr (C::REG > 0) {
-    // tile kt+1 waits in registers while tile kt is computed from LDS; at the
-    // end of the iteration it goes to the other LDS buffer and the registers
-    // are refilled with tile kt+2
     if (KT > 0) {
-      gload(0, 0);
-      wait_vmcnt<0>();
-      dswrite(0, 0);
-      if (KT > 1) gload(1, 0);
+      gload(0);
+      dswrite(0);
+      if (KT > 1) gload(1);
     }
   } else {
 #pragma unroll
     for (int s = 0; s < C::STAGES - 1; s++)
-      if (s < KT) issue(s, s);
+      if (s < KT) ld.issue(smem, s, s, wave);
+    if (KT >= C::STAGES - 1) {
+      wait_vmcnt<C::LOADS * (C::STAGES - 2)>();
+    } else {
+      wait_vmcnt<0>();
+    }
   }
+  __syncthreads();
+  if (KT > 0) read_slice(0, 0, qf[0], pf[0]);
 
-  auto ktile = [&](int kt) {
-    if constexpr (C::REG == 0) {
-      if (kt + C::STAGES - 2 < KT) {
-        wait_vmcnt<C::LOADS * (C::STAGES - 2)>();
-      } else {
-        wait_vmcnt<0>();
-      }
-    }
-    __syncthreads();
-    if constexpr (C::REG == 0) {
-      if (kt + C::STAGES - 1 < KT) issue(kt + C::STAGES - 1, (kt + C::STAGES - 1) % C::STAGES);
-    }
-
-    const FP8MLP_LDS char* sq = smem + (kt % C::STAGES) * C::STAGE_BYTES;
-    const FP8MLP_LDS char* sp = sq + C::Q_BYTES;
-    // Fragments are double-buffered across the k-slices of the tile: the LDS
-    // reads of slice s+1 are issued while the MFMAs of slice s run, and the
-    // scheduling groups interleave them one by one.
-    Frag qf[2][C::FM], pf[2][C::FN];
-#pragma unroll
-    for (int fm = 0; fm < C::FM; fm++) qf[0][fm] = load_q(sq, 0, fm);
-#pragma unroll
-    for (int fn = 0; fn < C::FN; fn++) pf[0][fn] = load_p(sp, 0, fn);
+  constexpr int NM = C::FM * C::FN;
+  constexpr int MEM_SLICE = C::REG ? C::SL - 2 : 0;
+  // LOAD: direct -- issue tile kt+STAGES-1; registers -- refill the VGPRs
+  // with tile kt+2.  NEXT: there is a tile kt+1 (registers: write it to LDS).
+  auto body = [&]<bool LOAD, bool NEXT>(int kt) {
+    const int stage = kt % C::STAGES, next_stage = (kt + 1) % C::STAGES;
 #pragma unroll
     for (int s = 0; s < C::SL; s++) {
+      if (s == C::SL - 1 && NEXT) {
+        if constexpr (C::REG == 0) {
+          if constexpr (LOAD) {
+            wait_vmcnt<C::LOADS * (C::STAGES - 2)>();
+          } else {
+            wait_vmcnt<0>();
+          }
+        }
+        // nothing crosses the barrier: the MFMAs of the last slice stay
+        // after it, where they cover the next tile's first reads
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (s + 1 < C::SL) {
-#pragma unroll
-        for (int fm = 0; fm < C::FM; fm++) qf[(s + 1) & 1][fm] = load_q(sq, s + 1, fm);
-#pragma unroll
-        for (int fn = 0; fn < C::FN; fn++) pf[(s + 1) & 1][fn] = load_p(sp, s + 1, fn);
+        read_slice(stage, s + 1, qf[(s + 1) & 1], pf[(s + 1) & 1]);
+      } else if (NEXT) {
+        read_slice(next_stage, 0, qf[0], pf[0]);
+      }
+      if (s == MEM_SLICE) {
+        if constexpr (C::REG == 0) {
+          if constexpr (LOAD) ld.issue(smem, kt + C::STAGES - 1, (kt + C::STAGES - 1) % C::STAGES, wave);
+        } else {
+          // (the compiler waits for each staging register before its write)
+          if constexpr (NEXT) dswrite((kt + 1) & 1);
+          if constexpr (LOAD) gload(kt + 2);
+        }
       }
 #pragma unroll
       for (int fm = 0; fm < C::FM; fm++)
 #pragma unroll
-        for (int fn = 0; fn < C::FN; fn++) acc[fm][fn] = mma(pf[s & 1][fn], qf[s & 1][fm], acc[fm][fn]);
-    }
-    sched_tile<C::FM * C::FN, NREADS, C::SL>();
-    if constexpr (C::REG > 0) {
-      if (kt + 1 < KT) {
-        wait_vmcnt<0>();
-        dswrite((kt + 1) & 1, 0);
-        if (kt + 2 < KT) gload(kt + 2, 0);
+        for (int fn = 0; fn < C::FN; fn++) acc[fm][fn] = mma<C>(pf[s & 1][fn], qf[s & 1][fm], acc[fm][fn]);
+      const bool reads = s + 1 < C::SL || NEXT;
+      const bool mem = s == MEM_SLICE;
+      if (reads && mem && (C::REG == 0 ? LOAD : NEXT)) {
+        if constexpr (C::REG == 0) {
+          sched_mix<NM, NREADS, 0, C::LOADS>();
+        } else {
+          sched_mix<NM, NREADS, C::LOADS, LOAD ? C::LOADS : 0>();
+        }
+      } else if (reads) {
+        sched_mix<NM, NREADS, 0, 0>();
+      } else {
+        sched_mix<NM, 0, 0, 0>();
       }
+      __builtin_amdgcn_sched_barrier(0);   // slices do not mix
     }
   };
-  for (int kt = 0; kt < KT; kt++) ktile(kt);
+  {
+    int kt = 0;
+    if constexpr (C::REG == 0) {
+      for (; kt + C::STAGES - 1 < KT; kt++) body.template operator()<true, true>(kt);
+      for (; kt + 1 < KT; kt++) body.template operator()<false, true>(kt);
+    } else {
+      for (; kt + 2 < KT; kt++) body.template operator()<true, true>(kt);
+      if (kt + 1 < KT) body.template operator()<false, true>(kt++);
+    }
+    if (kt < KT) body.template operator()<false, false>(kt);
+  }
 
-  TileCtx ctx{m0, n0, tm, tn, split, wm, wn, lane, a.M, a.N};
+  TileCtx ctx{t.m0, t.n0, t.tm, t.tn, t.split, wm, wn, lane, a.M, a.N};
+  epi.template run<C>(ctx, acc, smem);
+}
+
+// ------------------------------------------------------------------ kernel: two groups of 4 waves
+// 512 threads, one block per CU, 2 x 4 wave tiles.  Wave w belongs to group
+// g = w / 4 and shares its SIMD with wave w ^ 4 of the other group.  Each
+// wave's k-loop alternates two phases of equal length, separated by block
+// barriers, and the groups run one phase apart:
+//   M(j): read the fragments for the next HALF k-slices from LDS into
+//         registers; for even j also issue this wave's share of the global
+//         loads of the tile after the current one; for odd j wait for them;
+//   C(j): the MFMAs of those HALF k-slices, nothing else.
+// So in every phase one wave per SIMD only issues MFMAs while the other does
+// the memory work, and a stalled load or LDS instruction never holds up the
+// matrix core (a wave issues in order).  Tile s is read in the phases
+// 4s-1 .. 4s+2 (group 0 runs C(j) in phase 2j, group 1 in phase 2j+1); tile
+// s+1 goes into the other LDS buffer from phase 4s-1 on and is complete,
+// for every wave, at the barrier that ends phase 4s+2.
+template <class C, class Epi>
+__global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs a, Epi epi) {
+  static_assert(C::NW == 8 && C::STAGES == 2 && C::REG == 0 && C::OCC == 1, "two-group kernel");
+  static_assert(C::SL % 2 == 0, "k-slices split into two phases");
+  constexpr int EPI_BYTES = Epi::template lds_bytes<C>();
+  constexpr int SMEM = C::LDS_BYTES > EPI_BYTES ? C::LDS_BYTES : EPI_BYTES;
+  static_assert(SMEM <= 160 * 1024, "LDS with the epilogue's staging");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[SMEM];
+  FP8MLP_LDS char* smem = (FP8MLP_LDS char*)smem_raw;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int g = wave >> 2, wm = (wave >> 1) & 1, wn = 2 * (wave & 1) + g;
+
+  const TilePos t = tile_pos<C>(a);
+  const int KT = t.KT;
+  TileLoads<C> ld;
+  ld.init(a, t, wave, lane);
+  FragReader<C> fr;
+  fr.init(wm, wn, lane);
+  using Frag = typename FragT<C::ELT>::type;
+  constexpr int HALF = C::SL / 2;
+
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; i++)
+#pragma unroll
+    for (int j = 0; j < C::FN; j++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
+  Frag qf[HALF][C::FM], pf[HALF][C::FN];
+
+  // tile 0 in LDS for everyone, then group 1 sits out one phase
+  if (KT > 0) ld.issue(smem, 0, 0, wave);
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (g == 1) __syncthreads();
+
+  for (int j = 0; j < 2 * KT; j++) {
+    const int s = j >> 1, half = j & 1;
+    // ---- M(j)
+    {
+      const FP8MLP_LDS char* sq = smem + (s & 1) * C::STAGE_BYTES;
+      const FP8MLP_LDS char* sp = sq + C::Q_BYTES;
+#pragma unroll
+      for (int k = 0; k < HALF; k++) {
+#pragma unroll
+        for (int fm = 0; fm < C::FM; fm++) qf[k][fm] = fr.q(sq, half * HALF + k, fm);
+#pragma unroll
+        for (int fn = 0; fn < C::FN; fn++) pf[k][fn] = fr.p(sp, half * HALF + k, fn);
+      }
+      if (half == 0) {
+        if (s + 1 < KT) ld.issue(smem, s + 1, (s + 1) & 1, wave);
+      } else {
+        wait_vmcnt<0>();
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- C(j)
+#pragma unroll
+    for (int k = 0; k < HALF; k++)
+#pragma unroll
+      for (int fm = 0; fm < C::FM; fm++)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; fn++) acc[fm][fn] = mma<C>(pf[k][fn], qf[k][fm], acc[fm][fn]);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // group 0 matches group 1's extra barrier
+  if (g == 0) __syncthreads();
+
+  TileCtx ctx{t.m0, t.n0, t.tm, t.tn, t.split, wm, wn, lane, a.M, a.N};
   epi.template run<C>(ctx, acc, smem);
 }
 

@@ -26,7 +26,11 @@ inline int launch_gemm(const char* name, const GemmArgs& args, const Epi& epi, h
   GemmArgs a = args;
   a.group_m = tile_group_m(a.tiles_m, a.tiles_n, C::OCC);
   TraceScope trace(name, st);
-  hipLaunchKernelGGL((gemm_kernel<C, Epi>), dim3((unsigned)blocks), dim3(256), 0, st, a, epi);
+  if constexpr (C::NW == 8) {
+    hipLaunchKernelGGL((gemm_pp_kernel<C, Epi>), dim3((unsigned)blocks), dim3(C::NT), 0, st, a, epi);
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<C, Epi>), dim3((unsigned)blocks), dim3(C::NT), 0, st, a, epi);
+  }
   return launch_status();
 }
 

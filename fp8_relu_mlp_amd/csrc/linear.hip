@@ -13,7 +13,7 @@
 namespace fp8mlp {
 
 // Xq [M,K] e4m3 . Wt_q [K,N] e4m3 (transposing LDS reads)
-using CfgLin = GemmCfg<1, 192, 128, 128, 2, 2, KC, MNC, true>;
+using CfgLin = GemmCfg<1, 192, 128, 128, 2, 2, KC, MNC>;
 
 __global__ void k_zero_scalar(float* p) { *p = 0.0f; }
 

@@ -7,12 +7,15 @@
 
 namespace fp8mlp {
 
-// dY [M,d] . W2 [d,h]: W2 is k-major here, read with transposing LDS loads.
-using CfgDpost = GemmCfg<2, 256, 128, 64, 2, 2, KC, MNC, true>;
-// dpre [M,h] . W1 [h,d]
-using CfgDx = GemmCfg<2, 192, 128, 64, 2, 2, KC, MNC, true>;
-// dpre^T . X and dY^T . post: both operands are row-contiguous with k = token.
-using CfgDw = GemmCfg<2, 256, 128, 64, 2, 2, MNC, MNC, true>;
+// dY [M,d] . W2 [d,h]: W2 is k-major here, read with transposing LDS loads;
+// 256 x 256 tiles, two groups of four waves.
+using CfgDpost = GemmCfg<2, 256, 256, 128, 2, 1, KC, MNC, 0, 8>;
+// dpre [M,h] . W1 [h,d]: 192 x 256 tiles (d = 768 is three of them), two
+// groups of four waves taking turns at the matrix cores.
+using CfgDx = GemmCfg<2, 192, 256, 128, 2, 1, KC, MNC, 0, 8>;
+// dpre^T . X and dY^T . post: both operands are row-contiguous with k = token;
+// 256 x 256 tiles, two groups of four waves.
+using CfgDw = GemmCfg<2, 256, 256, 128, 2, 1, MNC, MNC, 0, 8>;
 
 struct BwdPlan {
   size_t dpre_bytes, part_bytes;

@@ -5,11 +5,11 @@
 
 namespace fp8mlp {
 
-// X [M,d] . W1[h,d]^T : both operands k-contiguous; 256 x 256 tiles, one block per CU,
-// direct global -> LDS loads.
-using CfgUp = GemmCfg<2, 256, 256, 128, 2, 1, KC, KC>;
+// X [M,d] . W1[h,d]^T : both operands k-contiguous; 256 x 256 tiles, two
+// groups of four waves taking turns at the matrix cores.
+using CfgUp = GemmCfg<2, 256, 256, 128, 2, 1, KC, KC, 0, 8>;
 // post_q [M,h] . W2t_q [h,d] : e4m3, the cache is read with transposing LDS loads.
-using CfgDown8 = GemmCfg<1, 192, 128, 128, 2, 2, KC, MNC, true>;
+using CfgDown8 = GemmCfg<1, 192, 128, 128, 2, 2, KC, MNC>;
 // post [M,h] . W2[d,h]^T : bf16 eval path.
 using CfgDownBf16 = GemmCfg<2, 192, 128, 64, 2, 2, KC, KC, true>;
 
