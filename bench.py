@@ -17,8 +17,12 @@ value = 12*M*d*h / t_step in TFLOP/s (the six GEMMs of forward + backward).
 One JSON line goes to stdout; progress goes to stderr.
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -31,6 +35,14 @@ PEAK_BF16 = 2500.0    # TFLOP/s, MI355X dense bf16 MFMA (published)
 PEAK_FP8 = 5000.0     # TFLOP/s, MI355X dense fp8 MFMA (published)
 PEAK_HBM = 8000.0     # GB/s
 METRIC = "MLP fwd+bwd TFLOP/s and % of MFMA peak, M=49152 d=768 h=3072, 1 GPU"
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "hbm_traffic_mlp_fwd_bwd_M49152.txt")
+# GEMM kernels carry the launch site as their last template argument
+KID_NAMES = {1: "up_gemm_relu2_quant", 2: "down_gemm_e4m3", 3: "down_gemm_bf16_eval", 4: "dpost_gemm_dpre",
+             5: "dx_gemm", 6: "dw1_gemm", 7: "dw2_gemm", 8: "fp8_linear_gemm"}
+OTHER_NAMES = {"k_max_final": "amax_final", "k_amax_partial": "amax_partial", "k_cast_transpose": "cast_transpose",
+               "k_splitk_reduce": "splitk_reduce", "k_quantize": "quantize_e4m3", "k_fill_zero": "fill_zero",
+               "k_zero_scalar": "zero_scalar", "k_scale_from_amax": "scale_from_amax", "k_max_small": "amax_small"}
 
 
 def log(msg):
@@ -55,6 +67,122 @@ def kernel_work(M, d, h):
 def mixed_floor_us(M, d, h):
     mdh = float(M) * d * h
     return (10 * mdh / (PEAK_BF16 * 1e12) + 2 * mdh / (PEAK_FP8 * 1e12)) * 1e6
+
+
+def kernel_source_hash():
+    """Digest of the kernel sources: HBM counters are valid only for the code they were taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp8_relu_mlp_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def logical_kernel_name(raw):
+    m = re.search(r"gemm\w*_kernel<.*, (\d+)>\(", raw)
+    if m:
+        return KID_NAMES.get(int(m.group(1)), raw)
+    m = re.search(r"fp8mlp::(k_\w+)", raw)
+    if m:
+        return OTHER_NAMES.get(m.group(1), m.group(1))
+    return raw
+
+
+def summarize_profiles(outdir):
+    """Turn the rocprofv3 runs under outdir (kt/: --kernel-trace --stats;
+    fetch/, write/: --pmc FETCH_SIZE / WRITE_SIZE of this benchmark; cfetch/,
+    cwrite/: the same counters for a plain 1 GiB device copy) into the text
+    summaries under profiles/."""
+    def rows(sub, pattern):
+        files = sorted(glob.glob(os.path.join(outdir, sub, "**", pattern), recursive=True))
+        if not files:
+            raise SystemExit(f"no {pattern} under {os.path.join(outdir, sub)}")
+        with open(files[0]) as fh:
+            return list(csv.DictReader(fh))
+
+    cmd_bench = "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extras"
+    # kernel trace: per-dispatch durations
+    trace = rows("kt", "*kernel_trace.csv")
+    dur = {}
+    for r in trace:
+        n = logical_kernel_name(r["Kernel_Name"])
+        dur.setdefault(n, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# Kernel durations: fused FP8 ReLU^2 MLP fwd+bwd, M=49152 d=768 h=3072 (one MI355X)", "",
+             "Command (from a scratch directory, TMPDIR=/tmp):", "",
+             f"    rocprofv3 --kernel-trace --stats --output-format csv -d OUT/kt -o kt -- {cmd_bench}", "",
+             "Summarised with `python3 bench.py --summarize-profiles OUT`.  Kernel names are the library's",
+             "launch sites (GEMM kernels carry the site as a template argument).  The run includes the",
+             "bootstrap forward and the warm-up steps.", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+    for n, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {n} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
+    lines += ["", f"Kernel sources digest: `{kernel_source_hash()}`"]
+    with open(os.path.join(PROFILES, "kernel_trace_mlp_fwd_bwd_M49152.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+    # HBM counters, scaled by what the same counter reads for a plain copy
+    def per_kernel(sub, counter):
+        acc = {}
+        for r in rows(sub, "*counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(logical_kernel_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    def copy_factor(sub, counter, true_bytes=1 << 30):
+        vals = [float(r["Counter_Value"]) * 1024.0 for r in rows(sub, "*counter_collection.csv")
+                if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
+        if not vals:
+            raise SystemExit(f"no copy dispatch in {sub}")
+        return true_bytes / (sum(vals) / len(vals)), sum(vals) / len(vals)
+
+    ff, fraw = copy_factor("cfetch", "FETCH_SIZE")
+    wf, wraw = copy_factor("cwrite", "WRITE_SIZE")
+    fetch, write = per_kernel("fetch", "FETCH_SIZE"), per_kernel("write", "WRITE_SIZE")
+    work = kernel_work(M, D, H)
+    table = {}
+    lines = ["# HBM traffic per launch: fused FP8 ReLU^2 MLP fwd+bwd, M=49152 d=768 h=3072 (one MI355X)", "",
+             "Commands (from a scratch directory, TMPDIR=/tmp; one counter per run):", "",
+             f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o f -- {cmd_bench}",
+             f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -o w -- {cmd_bench}",
+             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/cfetch -o f -- python3 bench.py --copy-calibration",
+             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/cwrite -o w -- python3 bench.py --copy-calibration",
+             "", "Calibration: a plain 1 GiB device-to-device copy reads "
+             f"FETCH_SIZE = {fraw / 2**20:.1f} MiB and WRITE_SIZE = {wraw / 2**20:.1f} MiB, so fetched bytes = "
+             f"{ff:.3f} x FETCH_SIZE and written bytes = {wf:.3f} x WRITE_SIZE.", "",
+             "| kernel | fetched MB | written MB | total MB | algorithmic MB | total / algorithmic |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for n in sorted(set(fetch) | set(write), key=lambda k: -(fetch.get(k, 0) + write.get(k, 0))):
+        fb, wb = ff * fetch.get(n, 0.0), wf * write.get(n, 0.0)
+        alg = work[n][1] if n in work else None
+        table[n] = {"fetch_bytes": round(fb), "write_bytes": round(wb)}
+        ratio = f"{(fb + wb) / alg:.2f}" if alg else ""
+        algs = f"{alg / 1e6:.1f}" if alg else ""
+        lines.append(f"| {n} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {(fb + wb) / 1e6:.1f} | {algs} | {ratio} |")
+    lines += ["", f"Kernel sources digest: `{kernel_source_hash()}`"]
+    with open(os.path.join(PROFILES, "hbm_traffic_mlp_fwd_bwd_M49152.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump({"src": kernel_source_hash(), "fetch_factor": ff, "write_factor": wf, "kernels": table}, fh,
+                  indent=1)
+        fh.write("\n")
+    print(f"wrote {PROFILES}/kernel_trace_mlp_fwd_bwd_M49152.md, hbm_traffic_mlp_fwd_bwd_M49152.md, {TRAFFIC_FILE}")
+
+
+def measured_traffic():
+    """Per-launch HBM bytes from the committed counter summary, or {} when
+    the kernels have changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return {}
+    if t.get("src") != kernel_source_hash():
+        return {}
+    return {k: v["fetch_bytes"] + v["write_bytes"] for k, v in t.get("kernels", {}).items()}
 
 
 def cpu_baseline(ins, amax_prev, target_s=15.0):
@@ -93,7 +221,12 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip the FP8-linear / eval / ablation lines")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (scales the HBM byte counters)")
+    ap.add_argument("--summarize-profiles", metavar="OUT",
+                    help="write the profiles/ summaries from the rocprofv3 runs under OUT (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); multi-GPU runs are not part of "
               "this build: the data-parallel sharding is described in DESIGN.md", file=sys.stderr)
@@ -172,6 +305,7 @@ def main():
     for name, t in kt.records():
         per.setdefault(name, []).append(t)
     work = kernel_work(M, D, H)
+    traffic = measured_traffic()
     kernels = {}
     for name, ts in per.items():
         avg_us = 1e3 * sum(ts) / len(ts)
@@ -180,13 +314,15 @@ def main():
             fl, by, peak = work[name]
             entry.update(tflops=round(fl / (avg_us * 1e-6) / 1e12, 1), frac_mfma=round(fl / (avg_us * 1e-6) / 1e12 / peak, 4),
                          hbm_gbs_alg=round(by / (avg_us * 1e-6) / 1e9, 1))
+        if name in traffic:
+            entry["hbm_bytes_measured"] = traffic[name]
         kernels[name] = entry
     gemms = [n for n in kernels if n in work]
     dom = max(gemms, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches_per_step"])
     fl, by, peak = work[dom]
     achieved = fl / (kernels[dom]["avg_us"] * 1e-6) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None,
+                "frac": round(achieved / peak, 4), "traffic": traffic.get(dom),
                 "algorithmic_flops_per_launch": fl, "algorithmic_bytes_per_launch": by}
 
     extras = {}

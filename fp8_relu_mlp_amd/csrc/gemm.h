@@ -35,6 +35,11 @@ namespace fp8mlp {
 
 enum { KC = 0, MNC = 1 };
 
+// Which contraction of the path a kernel instance serves.  It is a template
+// argument of the kernels only so that every launch site has its own kernel
+// symbol, which profilers report per symbol.
+enum : int { KID_UP = 1, KID_DOWN8, KID_DOWN_BF16, KID_DPOST, KID_DX, KID_DW1, KID_DW2, KID_LINEAR };
+
 template <int ELT_, int BM_, int BN_, int RB_, int STAGES_, int OCC_, int QL_, int PL_, int REG_ = 0, int NW_ = 4>
 struct GemmCfg {
   static constexpr int ELT = ELT_;                 // bytes per element: 2 bf16, 1 e4m3
@@ -412,7 +417,7 @@ __device__ __forceinline__ f32x16 mma(const typename FragT<C::ELT>::type& p, con
 }
 
 // ------------------------------------------------------------------ kernel: 4 waves
-template <class C, class Epi>
+template <class C, class Epi, int KID>
 __global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) {
   static_assert(C::NW == 4, "four-wave kernel");
   // the pipeline buffers, reused by the epilogue once the last tile is read
@@ -597,7 +602,7 @@ __global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) 
 // 4s-1 .. 4s+2 (group 0 runs C(j) in phase 2j, group 1 in phase 2j+1); tile
 // s+1 goes into the other LDS buffer from phase 4s-1 on and is complete,
 // for every wave, at the barrier that ends phase 4s+2.
-template <class C, class Epi>
+template <class C, class Epi, int KID>
 __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs a, Epi epi) {
   static_assert(C::NW == 8 && C::STAGES == 2 && C::REG == 0 && C::OCC == 1, "two-group kernel");
   static_assert(C::SL % 2 == 0, "k-slices split into two phases");

@@ -30,9 +30,9 @@ inline int launch_status() { return hip_status(hipGetLastError()); }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-#define FP8MLP_TRY(expr)                 \
+#define FP8MLP_TRY(...)                  \
   do {                                   \
-    int _st = (expr);                    \
+    int _st = (__VA_ARGS__);             \
     if (_st != FP8MLP_OK) return _st;    \
   } while (0)
 #define FP8MLP_REQUIRE(cond, status)     \

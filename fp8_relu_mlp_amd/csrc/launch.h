@@ -19,17 +19,31 @@ inline int tile_group_m(int tiles_m, int tiles_n, int occ) {
   return g;
 }
 
-template <class C, class Epi>
-inline int launch_gemm(const char* name, const GemmArgs& args, const Epi& epi, hipStream_t st) {
+inline const char* kid_name(int kid) {
+  switch (kid) {
+    case KID_UP: return "up_gemm_relu2_quant";
+    case KID_DOWN8: return "down_gemm_e4m3";
+    case KID_DOWN_BF16: return "down_gemm_bf16_eval";
+    case KID_DPOST: return "dpost_gemm_dpre";
+    case KID_DX: return "dx_gemm";
+    case KID_DW1: return "dw1_gemm";
+    case KID_DW2: return "dw2_gemm";
+    case KID_LINEAR: return "fp8_linear_gemm";
+  }
+  return "gemm";
+}
+
+template <class C, int KID, class Epi>
+inline int launch_gemm(const GemmArgs& args, const Epi& epi, hipStream_t st) {
   const int64_t blocks = (int64_t)args.tiles_m * args.tiles_n * args.splits;
   if (blocks == 0) return FP8MLP_OK;
   GemmArgs a = args;
   a.group_m = tile_group_m(a.tiles_m, a.tiles_n, C::OCC);
-  TraceScope trace(name, st);
+  TraceScope trace(kid_name(KID), st);
   if constexpr (C::NW == 8) {
-    hipLaunchKernelGGL((gemm_pp_kernel<C, Epi>), dim3((unsigned)blocks), dim3(C::NT), 0, st, a, epi);
+    hipLaunchKernelGGL((gemm_pp_kernel<C, Epi, KID>), dim3((unsigned)blocks), dim3(C::NT), 0, st, a, epi);
   } else {
-    hipLaunchKernelGGL((gemm_kernel<C, Epi>), dim3((unsigned)blocks), dim3(C::NT), 0, st, a, epi);
+    hipLaunchKernelGGL((gemm_kernel<C, Epi, KID>), dim3((unsigned)blocks), dim3(C::NT), 0, st, a, epi);
   }
   return launch_status();
 }

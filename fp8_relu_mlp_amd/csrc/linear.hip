@@ -88,7 +88,7 @@ int fp8_linear(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, con
   }
   GemmArgs a{Xq, K, Wt_q, N, M, N, K, (int)cdiv(M, CfgLin::BM), (int)cdiv(N, CfgLin::BN), 1, K, 0};
   EpiBf16Out epi{Y, N, 2, nullptr, 0.0f, x_scale, w_inv_scale};
-  return launch_gemm<CfgLin>("fp8_linear_gemm", a, epi, st);
+  return launch_gemm<CfgLin, KID_LINEAR>(a, epi, st);
 }
 
 }  // extern "C"

@@ -81,16 +81,17 @@ static int launch_zero(float* out, int64_t n, hipStream_t st) {
 }
 
 // One weight gradient C [Mo, No] = A^T B with A [K, Mo], B [K, No] (K = tokens).
-static int weight_grad(const char* name, const uint16_t* A, int64_t Mo, const uint16_t* B, int64_t No, int64_t K, float* out,
+template <int KID>
+static int weight_grad(const uint16_t* A, int64_t Mo, const uint16_t* B, int64_t No, int64_t K, float* out,
                        int accumulate, const BwdPlan& plan, float* part, hipStream_t st) {
   GemmArgs a{A, Mo, B, No, Mo, No, K, (int)cdiv(Mo, CfgDw::BM), (int)cdiv(No, CfgDw::BN), plan.splits,
              plan.k_per_split};
   if (plan.splits == 1) {
     EpiF32 epi{out, No, 0, accumulate};
-    return launch_gemm<CfgDw>(name, a, epi, st);
+    return launch_gemm<CfgDw, KID>(a, epi, st);
   }
   EpiF32 epi{part, No, Mo * No, 0};
-  FP8MLP_TRY(launch_gemm<CfgDw>(name, a, epi, st));
+  FP8MLP_TRY(launch_gemm<CfgDw, KID>(a, epi, st));
   return launch_reduce(part, plan.splits, Mo * No, out, accumulate, st);
 }
 
@@ -137,17 +138,17 @@ int mlp_relu2_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* W1, con
   {
     GemmArgs a{dY, d, W2, h, M, h, d, (int)cdiv(M, CfgDpost::BM), (int)cdiv(h, CfgDpost::BN), 1, d};
     EpiDpre epi{post, dpre, h};
-    FP8MLP_TRY(launch_gemm<CfgDpost>("dpost_gemm_dpre", a, epi, st));
+    FP8MLP_TRY(launch_gemm<CfgDpost, KID_DPOST>(a, epi, st));
   }
   // 2. dX = dpre W1
   {
     GemmArgs a{dpre, h, W1, d, M, d, h, (int)cdiv(M, CfgDx::BM), (int)cdiv(d, CfgDx::BN), 1, h};
     EpiBf16Out epi{dX, d, 0, nullptr, 0.0f, nullptr, nullptr};
-    FP8MLP_TRY(launch_gemm<CfgDx>("dx_gemm", a, epi, st));
+    FP8MLP_TRY(launch_gemm<CfgDx, KID_DX>(a, epi, st));
   }
   // 3. dW1 = dpre^T X ; 4. dW2 = dY^T post
-  FP8MLP_TRY(weight_grad("dw1_gemm", dpre, h, X, d, M, dW1, accumulate, plan, part, st));
-  FP8MLP_TRY(weight_grad("dw2_gemm", dY, d, post, h, M, dW2, accumulate, plan, part, st));
+  FP8MLP_TRY(weight_grad<KID_DW1>(dpre, h, X, d, M, dW1, accumulate, plan, part, st));
+  FP8MLP_TRY(weight_grad<KID_DW2>(dY, d, post, h, M, dW2, accumulate, plan, part, st));
   return FP8MLP_OK;
 }
 

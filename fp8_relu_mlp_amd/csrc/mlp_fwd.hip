@@ -72,7 +72,7 @@ int mlp_relu2_fwd(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t
   {
     GemmArgs a{X, d, W1, d, M, h, d, (int)plan.tm, (int)plan.tn, 1, d};
     EpiRelu2Quant epi{post, train ? post_q : nullptr, partial, amax_prev, margin, h, (int)plan.tn};
-    FP8MLP_TRY(launch_gemm<CfgUp>("up_gemm_relu2_quant", a, epi, st));
+    FP8MLP_TRY(launch_gemm<CfgUp, KID_UP>(a, epi, st));
   }
   // 2. reduce the partial amax tensor; record the scale that was used
   FP8MLP_TRY(launch_max_small(partial, plan.tm * plan.tn, amax_out, amax_prev, margin, train ? scale_out : nullptr,
@@ -81,11 +81,11 @@ int mlp_relu2_fwd(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t
   if (train) {
     GemmArgs a{post_q, h, W2t_q, d, M, d, h, (int)cdiv(M, CfgDown8::BM), (int)cdiv(d, CfgDown8::BN), 1, h};
     EpiBf16Out epi{Y, d, 1, amax_prev, margin, nullptr, w2_inv_scale};
-    FP8MLP_TRY(launch_gemm<CfgDown8>("down_gemm_e4m3", a, epi, st));
+    FP8MLP_TRY(launch_gemm<CfgDown8, KID_DOWN8>(a, epi, st));
   } else {
     GemmArgs a{post, h, W2, h, M, d, h, (int)cdiv(M, CfgDownBf16::BM), (int)cdiv(d, CfgDownBf16::BN), 1, h};
     EpiBf16Out epi{Y, d, 0, nullptr, 0.0f, nullptr, nullptr};
-    FP8MLP_TRY(launch_gemm<CfgDownBf16>("down_gemm_bf16_eval", a, epi, st));
+    FP8MLP_TRY(launch_gemm<CfgDownBf16, KID_DOWN_BF16>(a, epi, st));
   }
   return FP8MLP_OK;
 }
