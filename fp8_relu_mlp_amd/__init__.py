@@ -8,9 +8,11 @@ is not built, the first call raises.
 
 Entry points (same names as the C ABI):
   mlp_relu2_fwd, mlp_relu2_bwd, fp8_cast_transpose, fp8_cast_transpose_w2,
-  amax_reduce, fp8_scale_from_amax, fp8_linear
+  amax_reduce, fp8_scale_from_amax, fp8_linear, and the layer-stack helpers
+  rmsnorm_fwd, rmsnorm_bwd, add_bf16, sgd_update_bf16
 and ``Relu2MLP``, one MLP block's device state (bf16 weights, the transposed
-fp8 W2 cache with its scales, the delayed-scale amax carried between steps).
+fp8 W2 cache with its scales, the delayed-scale amax carried between steps);
+``stack.Relu2Stack`` trains a stack of such blocks.
 """
 import torch
 
@@ -22,7 +24,8 @@ F32 = 0
 BF16 = 1
 
 __all__ = ["mlp_relu2_fwd", "mlp_relu2_bwd", "fp8_cast_transpose", "fp8_cast_transpose_w2", "amax_reduce",
-           "fp8_scale_from_amax", "fp8_linear", "Relu2MLP", "KernelTimer", "Fp8MlpError", "TRAIN_FP8", "EVAL_BF16"]
+           "fp8_scale_from_amax", "fp8_linear", "rmsnorm_fwd", "rmsnorm_bwd", "add_bf16", "sgd_update_bf16",
+           "Relu2MLP", "KernelTimer", "Fp8MlpError", "TRAIN_FP8", "EVAL_BF16"]
 
 
 def _p(t):
@@ -125,6 +128,31 @@ def fp8_linear(X, x_scale, Wt_q, w_inv_scale, Y, x_amax_out=None, workspace=None
     check("fp8_linear", L.fp8_linear(
         _p(X), _p(x_scale), _p(Wt_q), _p(w_inv_scale), _p(Y), _p(x_amax_out), M, K, N, _p(ws), wsb,
         _stream(stream)))
+
+
+def rmsnorm_fwd(x, xn, inv_rms, eps=1e-6, stream=None):
+    """xn = bf16(x * r), r = 1/sqrt(mean(x^2) + eps) per row -> inv_rms [M] fp32."""
+    M, d = x.shape
+    check("rmsnorm_fwd", lib().rmsnorm_fwd(_p(x), _p(xn), _p(inv_rms), M, d, float(eps), _stream(stream)))
+
+
+def rmsnorm_bwd(x, inv_rms, dxn, g_in, g_out, stream=None):
+    """g_out = bf16(g_in + RMSNorm backward of dxn) per row."""
+    M, d = x.shape
+    check("rmsnorm_bwd", lib().rmsnorm_bwd(_p(x), _p(inv_rms), _p(dxn), _p(g_in), _p(g_out), M, d,
+                                           _stream(stream)))
+
+
+def add_bf16(a, b, out, stream=None):
+    """out = bf16(a + b) elementwise."""
+    check("add_bf16", lib().add_bf16(_p(a), _p(b), _p(out), a.numel(), _stream(stream)))
+
+
+def sgd_update_bf16(W, dW, lr, stream=None):
+    """W = bf16(W - fp32(lr * dW)) in place (W bf16, dW fp32)."""
+    if W.numel() != dW.numel():
+        raise ValueError("W and dW sizes differ")
+    check("sgd_update_bf16", lib().sgd_update_bf16(_p(W), _p(dW), W.numel(), float(lr), _stream(stream)))
 
 
 class KernelTimer:

@@ -36,6 +36,10 @@ SIGNATURES = {
     "fp8_scale_from_amax": (c_int, [vp, c_float, vp, vp, vp]),
     "fp8_linear_workspace": (c_size, [c_i64, c_i64]),
     "fp8_linear": (c_int, [vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, vp, c_size, vp]),
+    "rmsnorm_fwd": (c_int, [vp, vp, vp, c_i64, c_i64, c_float, vp]),
+    "rmsnorm_bwd": (c_int, [vp, vp, vp, vp, vp, c_i64, c_i64, vp]),
+    "add_bf16": (c_int, [vp, vp, vp, c_i64, vp]),
+    "sgd_update_bf16": (c_int, [vp, vp, c_i64, c_float, vp]),
     "fp8mlp_timing_start": (c_int, [c_int]),
     "fp8mlp_timing_stop": (c_int, []),
     "fp8mlp_timing_get": (c_int, [c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(c_float)]),

@@ -28,6 +28,7 @@ WORKLOADS = {
     "fwdbwd": (49152, 768, 3072, 2),      # forward + backward, the timed workload
     "stack": (65536, 768, 3072, 4),       # 12 layers x 8 steps with state carry
 }
+STACK = {"layers": 12, "steps": 8, "lr": 1e-3}
 ATTN = {"M": 49152, "d": 768, "qkv": 2304, "seed": 3}
 
 
@@ -84,6 +85,20 @@ def perturbed_w1(W1_bits, seed):
     w = torch.from_numpy(W1_bits.view(np.int16).copy()).view(torch.bfloat16).float()
     w = w + torch.from_numpy(delta)
     return w.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def stack_weights(L, d, h, seed):
+    """Per-layer weights of the layer-stack workload: W1 [h,d] ~ N(0,1/d),
+    W2 [d,h] ~ N(0,1/h), one named stream per layer and matrix."""
+    return [(normal_bf16((h, d), 1.0 / d, seed, f"W1.{l}"), normal_bf16((d, h), 1.0 / h, seed, f"W2.{l}"))
+            for l in range(L)]
+
+
+def stack_batch(M, d, seed, step):
+    """Batch of one step of the layer-stack workload: X [M,d] ~ N(0,1) and
+    the top gradient dY [M,d] ~ N(0,1e-3)."""
+    return {"X": normal_bf16((M, d), 1.0, seed, f"stack.X.{step}"),
+            "dY": normal_bf16((M, d), 1e-3, seed, f"stack.dY.{step}")}
 
 
 def attn_inputs(M=None, d=None, qkv=None, seed=None):

@@ -192,6 +192,36 @@ int fp8_linear(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, con
                size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Layer-stack helpers.  The speedrun pages train the MLP block inside a
+ * pre-norm transformer and carry its FP8 state per layer from step to step
+ * ("A Retrospective on Our World Records", Main Track: delayed scaling from
+ * amax(t-1); the transposed FP8 W2 cache refreshed after each optimizer
+ * update).  These calls let the block be trained as a stack
+ * x <- x + MLP(rmsnorm(x)); the pages give no formulas for them, so they
+ * follow the plain textbook definitions (weightless RMSNorm, SGD):
+ *
+ * rmsnorm_fwd:  per row of x [M, d] bf16:
+ *     r = 1 / sqrt(sum_j(x_j^2) / d + eps)   (fp32; -> inv_rms [M] fp32)
+ *     xn = bf16(x * r)                       (-> xn [M, d] bf16)
+ * rmsnorm_bwd:  per row, given dxn = dL/dxn [M, d] bf16 and the stream
+ *   gradient g_in [M, d] bf16 of the residual that bypasses the block:
+ *     xh = x * r;  dx = r * (dxn - xh * sum_j(dxn_j xh_j) / d)
+ *     g_out = bf16(g_in + dx)                (g_out may alias g_in)
+ * add_bf16:     out[i] = bf16(a[i] + b[i])   (the residual add; out may
+ *   alias a or b)
+ * sgd_update_bf16:  W[i] = bf16(fp32(W[i] - fp32(lr * dW[i]))), in place,
+ *   W bf16, dW fp32 (the weight gradients of mlp_relu2_bwd)
+ * Sizes: d and n multiples of 8; M >= 0 and n >= 0 (0 launches nothing).
+ * Pointers 16-byte aligned (inv_rms 4-byte aligned).  eps >= 0.
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_ARCH, E_ARG, E_HIP.
+ * ---------------------------------------------------------------------- */
+int rmsnorm_fwd(const uint16_t* x, uint16_t* xn, float* inv_rms, int64_t M, int64_t d, float eps, void* stream);
+int rmsnorm_bwd(const uint16_t* x, const float* inv_rms, const uint16_t* dxn, const uint16_t* g_in, uint16_t* g_out,
+                int64_t M, int64_t d, void* stream);
+int add_bf16(const uint16_t* a, const uint16_t* b, uint16_t* out, int64_t n, void* stream);
+int sgd_update_bf16(uint16_t* W, const float* dW, int64_t n, float lr, void* stream);
+
+/* ------------------------------------------------------------------------
  * Per-kernel timing (benchmarking / profiling aid, not part of the method).
  * fp8mlp_timing_start(capacity) creates up to `capacity` hipEvent pairs
  * (driver objects, no device memory) and, until fp8mlp_timing_stop(), brackets

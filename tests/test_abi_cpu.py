@@ -116,3 +116,19 @@ def test_bwd_and_misc_validation(L):
     assert lin(Y=17) == E_ALIGN
     assert lin(ws=None) == E_WS
     assert lin(wsb=100) == E_WS
+
+
+def test_stack_helpers_validation(L):
+    assert L.rmsnorm_fwd(16, 16, 16, 4, 100, 1e-6, None) == E_SHAPE     # d % 8
+    assert L.rmsnorm_fwd(16, 16, 16, -1, 64, 1e-6, None) == E_SHAPE
+    assert L.rmsnorm_fwd(16, 16, 16, 4, 64, -1.0, None) == E_ARG
+    assert L.rmsnorm_fwd(None, 16, 16, 4, 64, 1e-6, None) == E_NULL
+    assert L.rmsnorm_fwd(16, 24, 16, 4, 64, 1e-6, None) == E_ALIGN
+    assert L.rmsnorm_fwd(None, None, None, 0, 64, 1e-6, None) == OK       # empty: nothing to do
+    assert L.rmsnorm_bwd(16, 16, 16, None, 16, 4, 64, None) == E_NULL
+    assert L.rmsnorm_bwd(16, 18, 16, 16, 16, 4, 64, None) == E_ALIGN     # inv_rms 4-byte aligned
+    assert L.add_bf16(16, 16, 16, 12, None) == E_SHAPE
+    assert L.add_bf16(16, None, 16, 16, None) == E_NULL
+    assert L.sgd_update_bf16(16, 16, 12, 1e-3, None) == E_SHAPE
+    assert L.sgd_update_bf16(16, 16, 16, float("nan"), None) == E_ARG
+    assert L.sgd_update_bf16(16, 40, 16, 1e-3, None) == E_ALIGN
