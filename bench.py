@@ -205,7 +205,7 @@ def cpu_baseline(ins, amax_prev, target_s=15.0):
         return time.perf_counter() - t0
 
     t1 = run(512)
-    ms = int(min(16384, max(512, 512 * target_s / max(t1, 1e-3))) // 512 * 512)
+    ms = int(min(M, max(512, 512 * target_s / max(t1, 1e-3))) // 512 * 512)
     t = run(ms)
     return {"value": 12.0 * ms * D * H / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"first {ms} of {M} token rows (d={D}, h={H}), fwd+bwd+W2 refresh, {t:.1f} s",
@@ -353,8 +353,10 @@ def main():
 
 def extra_measurements(fm, torch, dev, X, W2, blk, post, post_q, Y, ws_f, reps=20):
     """Side measurements (not part of `value`): forward-only TRAIN vs EVAL
-    (bf16 down-projection ablation), the FP8 attention projections and the
-    W2 cache refresh."""
+    (bf16 down-projection ablation), the W2 cache refresh, the layer-stack
+    workload (12 layers x 8 SGD steps at M=65536, with the share of post
+    values the e4m3 copy clipped per layer and step) and the FP8 attention
+    projections."""
     import numpy as np
     from fp8_relu_mlp_amd import synth
 
@@ -382,6 +384,45 @@ def extra_measurements(fm, torch, dev, X, W2, blk, post, post_q, Y, ws_f, reps=2
                                                   workspace=ws_c))
     out["w2_refresh_us"] = round(t_w2 * 1e3, 2)
     out["w2_refresh_gbs_alg"] = round((D * H * 2 * 2 + D * H) / (t_w2 * 1e-3) / 1e9, 1)
+
+    # layer-stack workload: 12 layers x 8 SGD steps at M=65536 (state carry per layer)
+    from fp8_relu_mlp_amd.stack import Relu2Stack
+    Ms, ds, hs, seed_s = synth.WORKLOADS["stack"]
+    Ls, steps_s = synth.STACK["layers"], synth.STACK["steps"]
+
+    def bfd(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    wts = synth.stack_weights(Ls, ds, hs, seed_s)
+    batches = [synth.stack_batch(Ms, ds, seed_s, t) for t in range(steps_s)]
+    Xs = [bfd(b["X"]) for b in batches]
+    dYs = [bfd(b["dY"]) for b in batches]
+
+    def stack_run(clip=None):
+        stk = Relu2Stack([bfd(w1) for w1, _ in wts], [bfd(w2) for _, w2 in wts], lr=synth.STACK["lr"])
+        stk.step(Xs[0], dYs[0])            # allocation + the bootstrap step, untimed
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for t in range(steps_s):
+            stk.step(Xs[t], dYs[t])
+            if clip is not None:
+                clip.append([stk.clip_fraction(l) for l in range(Ls)])
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    t_stack = stack_run()
+    clip = []
+    stack_run(clip)
+    fl_stack = 12.0 * Ms * ds * hs * Ls * steps_s
+    floor_stack = steps_s * Ls * mixed_floor_us(Ms, ds, hs) / 1e3
+    out["stack_12x8_ms"] = round(t_stack, 2)
+    out["stack_12x8_tflops"] = round(fl_stack / (t_stack * 1e-3) / 1e12, 1)
+    out["stack_12x8_mixed_floor_ms"] = round(floor_stack, 2)
+    out["stack_clip_fraction_max"] = max(max(r) for r in clip)
+    out["stack_clip_fraction_nonzero_layer_steps"] = sum(1 for r in clip for v in r if v > 0)
+    del Xs, dYs
 
     # FP8 attention projections: QKV [49152,768]x[768,2304], O [49152,768]x[768,768]
     a = synth.attn_inputs()
