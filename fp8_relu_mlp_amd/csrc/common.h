@@ -64,6 +64,16 @@ __device__ __forceinline__ uint32_t pack_e4m3x4_nonneg(float a, float b, float c
   return u - (z >> 7);                                        // 0x7F -> 0x7E, no borrow
 }
 
+// e4m3 codes of four values known to lie in [+0, 464] (no NaN): the
+// converter's round-to-nearest-even result needs no saturation fix-up there
+// ((448, 464] already rounds to 0x7E).  The first conversion's other half is
+// overwritten by the second, so any register serves as its "old" operand.
+__device__ __forceinline__ uint32_t pack_e4m3x4_inrange(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
 // Keeps the compiler from re-deriving a value from its operands (the packed
 // bf16 word below would otherwise be re-converted value by value).
 __device__ __forceinline__ uint32_t opaque(uint32_t x) {
@@ -124,6 +134,15 @@ __device__ __forceinline__ void store_stream(void* p, uint4 v) {
 }
 __device__ __forceinline__ void store_stream(void* p, uint2 v) {
   __builtin_nontemporal_store(i32x2{(int)v.x, (int)v.y}, (i32x2*)p);
+}
+
+// Non-temporal buffer stores at a 32-bit byte offset from a resource's base;
+// offsets at or past the resource's size are dropped by the hardware.
+__device__ __forceinline__ void buffer_store_stream16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, r, off, 0, 2 /* nt */);
+}
+__device__ __forceinline__ void buffer_store_stream8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)v.x, (int)v.y}, r, off, 0, 2 /* nt */);
 }
 
 // s_waitcnt vmcnt(n) with the other counters left unconstrained (gfx9 encoding).

@@ -57,6 +57,36 @@ struct Tile16 {
       if (m < c.M && n < c.N) f(m, n, v);
     }
   }
+  // The same sweep for a tile that lies wholly inside the matrix, without
+  // bounds checks: f(p, 16 bytes) for pass p, in which this thread holds
+  // tile row row0() + p * ROWS_PER_PASS, chunk chunk0().
+  static constexpr int ROWS_PER_PASS = C::NT / CPR;
+  static_assert(C::NT % CPR == 0, "whole rows per pass");
+  static_assert(ROWS_PER_PASS % (XM + 1) == 0, "passes keep the row swizzle");
+  __device__ static __forceinline__ int row0() { return (int)threadIdx.x / CPR; }
+  __device__ static __forceinline__ int chunk0() { return (int)threadIdx.x % CPR; }
+  template <class F>
+  __device__ static __forceinline__ void rows_interior(const FP8MLP_LDS char* s, F&& f) {
+    const uint32_t o = off(row0(), chunk0());
+#pragma unroll
+    for (int p = 0; p < PASSES; p++) {
+      // rows of a pass are ROWS_PER_PASS apart, a multiple of the swizzle period
+      const i32x4 r = lds_read_b128(s, o + (uint32_t)(p * ROWS_PER_PASS * CPR * 16));
+      f(p, uint4{(uint32_t)r[0], (uint32_t)r[1], (uint32_t)r[2], (uint32_t)r[3]});
+    }
+  }
+  // The LDS image -> the 16-bit matrix g (leading dimension ld), row by row,
+  // with streaming stores; tiles inside the matrix skip the bounds checks.
+  __device__ static __forceinline__ void store(const FP8MLP_LDS char* s, const TileCtx& c, uint16_t* g, int64_t ld) {
+    if (c.m0 + C::BM <= c.M && c.n0 + C::BN <= c.N) {
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(g + c.m0 * ld + c.n0, (uint64_t)C::BM * ld * 2);
+      const uint32_t o = (uint32_t)row0() * (uint32_t)ld * 2 + chunk0() * 16;
+      const uint32_t step = (uint32_t)ROWS_PER_PASS * (uint32_t)ld * 2;
+      rows_interior(s, [&](int p, uint4 v) { buffer_store_stream16(r, o + p * step, v); });
+    } else {
+      rows(s, c, [&](int64_t m, int64_t n, uint4 v) { store_stream(g + m * ld + n, v); });
+    }
+  }
   // Global 16-bit matrix (leading dimension ld) -> LDS image, loaded straight
   // into LDS in row order (streaming: read once); rows past the matrix end
   // read as zero.
@@ -107,41 +137,87 @@ struct EpiRelu2Quant {
     using T = Tile16<C>;
     const float s = post_q ? scale_from_amax(*amax_prev, margin) : 1.0f;
     uint32_t mx = 0;   // two running 16-bit maxima
+    const bool interior = c.m0 + C::BM <= c.M && c.n0 + C::BN <= c.N;
     __syncthreads();   // every wave is done with the last pipeline stage
+    // fragments -> bf16 post in the LDS image; the maximum skips values
+    // outside the matrix (edge tiles only)
+    auto frags = [&]<bool EDGE>() {
 #pragma unroll
-    for (int fm = 0; fm < C::FM; fm++) {
-      const bool row_in = c.m0 + T::frag_row(c, fm) < c.M;
+      for (int fm = 0; fm < C::FM; fm++) {
+        const bool row_in = !EDGE || c.m0 + T::frag_row(c, fm) < c.M;
 #pragma unroll
-      for (int fn = 0; fn < C::FN; fn++) {
-        uint32_t pk[8];
+        for (int fn = 0; fn < C::FN; fn++) {
+          uint32_t pk[8];
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) pk[e / 2] = pack_bf16x2(relu_sq(acc[fm][fn][e]), relu_sq(acc[fm][fn][e + 1]));
-        if (row_in && c.n0 + T::frag_chunk(c, fn) * 8 < c.N) {
+          for (int e = 0; e < 16; e += 2)
+            pk[e / 2] = opaque(pack_bf16x2(relu_sq(acc[fm][fn][e]), relu_sq(acc[fm][fn][e + 1])));
+          if (!EDGE || (row_in && c.n0 + T::frag_chunk(c, fn) * 8 < c.N)) {
 #pragma unroll
-          for (int i = 0; i < 8; i++) mx = max_u16x2(mx, pk[i]);
+            for (int i = 0; i < 8; i++) mx = max_u16x2(mx, pk[i]);
+          }
+          T::put(smem, c, fm, fn, pk);
         }
-        T::put(smem, c, fm, fn, pk);
       }
+    };
+    if (interior) {
+      frags.template operator()<false>();
+    } else {
+      frags.template operator()<true>();
     }
     mx = (mx >> 16) > (mx & 0xffffu) ? (mx >> 16) : (mx & 0xffffu);
     mx = wave_max_u32(mx);
     uint32_t* red = (uint32_t*)(smem + T::BYTES);
     if (c.lane == 0) red[threadIdx.x >> 6] = mx;
     __syncthreads();
-    T::rows(smem, c, [&](int64_t m, int64_t n, uint4 v) {
-      store_stream(post + m * ld + n, v);
-      if (post_q) {
-        uint2 q;
-        q.x = pack_e4m3x4_nonneg(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
-        q.y = pack_e4m3x4_nonneg(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
-        store_stream(post_q + m * ld + n, q);
+    uint32_t m4 = red[0];
+#pragma unroll
+    for (int i = 1; i < C::NW; i++) m4 = red[i] > m4 ? red[i] : m4;
+    const float tile_max = __uint_as_float(m4 << 16);
+    if (interior) {
+      // interior tile: 32-bit offsets from the tile origin, no bounds checks
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(post + c.m0 * ld + c.n0, (uint64_t)C::BM * ld * 2);
+      // byte offsets of this thread's chunk in pass 0 and the per-pass step
+      const uint32_t op = (uint32_t)T::row0() * (uint32_t)ld * 2 + T::chunk0() * 16;
+      const uint32_t oq = (uint32_t)T::row0() * (uint32_t)ld + T::chunk0() * 8;
+      const uint32_t sp = (uint32_t)T::ROWS_PER_PASS * (uint32_t)ld * 2, sq = sp / 2;
+      if (!post_q) {
+        T::rows_interior(smem, [&](int p, uint4 v) { buffer_store_stream16(rp, op + p * sp, v); });
+      } else {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(post_q + c.m0 * ld + c.n0, (uint64_t)C::BM * ld);
+        // Every post value of the tile is <= tile_max, and rounding is
+        // monotone, so fp32(tile_max * s) <= 464 means no product of the tile
+        // reaches the range the converter does not saturate by itself
+        // (NaN and inf fail the test and take the general encode).
+        if (tile_max * s <= 464.0f) {
+          T::rows_interior(smem, [&](int p, uint4 v) {
+            buffer_store_stream16(rp, op + p * sp, v);
+            uint2 q;
+            q.x = pack_e4m3x4_inrange(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
+            q.y = pack_e4m3x4_inrange(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
+            buffer_store_stream8(rq, oq + p * sq, q);
+          });
+        } else {
+          T::rows_interior(smem, [&](int p, uint4 v) {
+            buffer_store_stream16(rp, op + p * sp, v);
+            uint2 q;
+            q.x = pack_e4m3x4_nonneg(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
+            q.y = pack_e4m3x4_nonneg(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
+            buffer_store_stream8(rq, oq + p * sq, q);
+          });
+        }
       }
-    });
-    if (threadIdx.x == 0) {
-      uint32_t m4 = red[0];
-      for (int i = 1; i < C::NW; i++) m4 = red[i] > m4 ? red[i] : m4;
-      partial[c.tm * tiles_n + c.tn] = __uint_as_float(m4 << 16);
+    } else {
+      T::rows(smem, c, [&](int64_t m, int64_t n, uint4 v) {
+        store_stream(post + m * ld + n, v);
+        if (post_q) {
+          uint2 q;
+          q.x = pack_e4m3x4_nonneg(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
+          q.y = pack_e4m3x4_nonneg(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
+          store_stream(post_q + m * ld + n, q);
+        }
+      });
     }
+    if (threadIdx.x == 0) partial[c.tm * tiles_n + c.tn] = tile_max;
   }
 };
 
@@ -187,7 +263,7 @@ struct EpiBf16Out {
       }
     }
     __syncthreads();
-    T::rows(smem, c, [&](int64_t m, int64_t n, uint4 v) { store_stream(y + m * ld + n, v); });
+    T::store(smem, c, y, ld);
   }
 };
 
@@ -235,7 +311,7 @@ struct EpiDpre {
       }
     }
     __syncthreads();
-    T::rows(smem, c, [&](int64_t m, int64_t n, uint4 v) { store_stream(dpre + m * ld + n, v); });
+    T::store(smem, c, dpre, ld);
   }
 };
 
