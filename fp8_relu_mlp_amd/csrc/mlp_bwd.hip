@@ -3,22 +3,24 @@
 //   dX    = dpre W1          bf16 out
 //   dW1   = dpre^T X         fp32, split-k over M, reduced in split order
 //   dW2   = dY^T post        fp32, split-k over M, reduced in split order
+// W1 and W2 are first transposed into the workspace (4.7 MB each at the
+// GPT-2-small shape) so that both dgrad GEMMs read k-contiguous operands
+// with plain 16-byte LDS reads.
 #include "launch.h"
 
 namespace fp8mlp {
 
-// dY [M,d] . W2 [d,h]: W2 is k-major here, read with transposing LDS loads;
-// 256 x 256 tiles, two groups of four waves.
-using CfgDpost = GemmCfg<2, 256, 256, 128, 2, 1, KC, MNC, 0, 8>;
-// dpre [M,h] . W1 [h,d]: 192 x 256 tiles (d = 768 is three of them), two
-// groups of four waves taking turns at the matrix cores.
-using CfgDx = GemmCfg<2, 192, 256, 128, 2, 1, KC, MNC, 0, 8>;
+// dY [M,d] . W2t [h,d]^T: 256 x 256 tiles, two groups of four waves.
+using CfgDpost = GemmCfg<2, 256, 256, 128, 2, 1, KC, KC, 0, 8>;
+// dpre [M,h] . W1t [d,h]^T: 192 x 256 tiles (d = 768 is three of them, and
+// M = 49152 gives exactly three rounds of 256 blocks).
+using CfgDx = GemmCfg<2, 192, 256, 128, 2, 1, KC, KC, 0, 8>;
 // dpre^T . X and dY^T . post: both operands are row-contiguous with k = token;
 // 256 x 256 tiles, two groups of four waves.
 using CfgDw = GemmCfg<2, 256, 256, 128, 2, 1, MNC, MNC, 0, 8>;
 
 struct BwdPlan {
-  size_t dpre_bytes, part_bytes;
+  size_t dpre_bytes, wt_bytes, part_bytes;   // dpre; W1t + W2t; split-k partials of dW
   int splits;
   int64_t k_per_split;
 };
@@ -26,6 +28,7 @@ struct BwdPlan {
 static BwdPlan bwd_plan(int64_t M, int64_t d, int64_t h) {
   BwdPlan p;
   p.dpre_bytes = align_up((size_t)(M * h) * 2, 256);
+  p.wt_bytes = 2 * align_up((size_t)(h * d) * 2, 256);
   const int64_t tiles = cdiv(h, CfgDw::BM) * cdiv(d, CfgDw::BN);
   // about two rounds of blocks over 256 CUs x OCC resident blocks
   int64_t s = (256 * CfgDw::OCC * 2 + tiles - 1) / (tiles > 0 ? tiles : 1) / 2;
@@ -37,6 +40,52 @@ static BwdPlan bwd_plan(int64_t M, int64_t d, int64_t h) {
   p.splits = (int)(M > 0 ? cdiv(M, p.k_per_split) : 1);
   p.part_bytes = p.splits > 1 ? align_up((size_t)p.splits * (size_t)(h * d) * 4, 256) : 0;
   return p;
+}
+
+// W1t [d, h] = W1 [h, d]^T (blockIdx.z = 0) and W2t [h, d] = W2 [d, h]^T
+// (blockIdx.z = 1) in one launch, 64 x 64 bf16 tiles through LDS (d and h
+// are multiples of 64).
+__global__ void __launch_bounds__(256) k_transpose_weights(const uint16_t* __restrict__ W1,
+                                                           const uint16_t* __restrict__ W2, int64_t d, int64_t h,
+                                                           uint16_t* __restrict__ W1t, uint16_t* __restrict__ W2t) {
+  __shared__ uint16_t tile[64][64 + 2];   // [c][r]
+  const bool second = blockIdx.z == 1;
+  const uint16_t* src = second ? W2 : W1;
+  uint16_t* dst = second ? W2t : W1t;
+  const int64_t R = second ? d : h, C = second ? h : d;   // src is [R, C]
+  // the grid covers max(d, h) / 64 tiles in each direction; skip the excess
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  if (r0 >= R || c0 >= C) return;
+#pragma unroll
+  for (int it = 0; it < 2; it++) {
+    const int i = threadIdx.x + it * 256;
+    const int r = i >> 3, ch = i & 7;
+    const uint4 v = *(const uint4*)(src + (r0 + r) * C + c0 + ch * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      tile[ch * 8 + 2 * e][r] = (uint16_t)(w[e] & 0xffffu);
+      tile[ch * 8 + 2 * e + 1][r] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 2; it++) {
+    const int i = threadIdx.x + it * 256;
+    const int c = i >> 3, ch = i & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) w[e] = (uint32_t)tile[c][ch * 8 + 2 * e] | ((uint32_t)tile[c][ch * 8 + 2 * e + 1] << 16);
+    *(uint4*)(dst + (c0 + c) * R + r0 + ch * 8) = uint4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+static int launch_transpose_weights(const uint16_t* W1, const uint16_t* W2, int64_t d, int64_t h, uint16_t* W1t,
+                                    uint16_t* W2t, hipStream_t st) {
+  const unsigned g = (unsigned)((d > h ? d : h) / 64);
+  TraceScope trace("transpose_weights", st);
+  hipLaunchKernelGGL(k_transpose_weights, dim3(g, g, 2), dim3(256), 0, st, W1, W2, d, h, W1t, W2t);
+  return launch_status();
 }
 
 // out[i] = (accumulate ? out[i] : 0) + part[0][i] + part[1][i] + ... in split order.
@@ -104,7 +153,7 @@ extern "C" {
 size_t mlp_relu2_bwd_workspace(int64_t M, int64_t d, int64_t h) {
   if (M < 0 || d <= 0 || h <= 0) return 0;
   const BwdPlan p = bwd_plan(M, d, h);
-  return p.dpre_bytes + p.part_bytes;
+  return p.dpre_bytes + p.wt_bytes + p.part_bytes;
 }
 
 int mlp_relu2_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* W1, const uint16_t* W2,
@@ -118,7 +167,7 @@ int mlp_relu2_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* W1, con
                         (const void*)dX, (const void*)dW1, (const void*)dW2})
     FP8MLP_REQUIRE(p == nullptr || aligned16(p), FP8MLP_E_ALIGN);
   const BwdPlan plan = bwd_plan(M, d, h);
-  const size_t need = plan.dpre_bytes + plan.part_bytes;
+  const size_t need = plan.dpre_bytes + plan.wt_bytes + plan.part_bytes;
   FP8MLP_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), FP8MLP_E_WORKSPACE);
   FP8MLP_REQUIRE(need == 0 || aligned16(workspace), FP8MLP_E_ALIGN);
   FP8MLP_TRY(check_device());
@@ -132,17 +181,20 @@ int mlp_relu2_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* W1, con
     return FP8MLP_OK;
   }
   uint16_t* dpre = (uint16_t*)workspace;
-  float* part = (float*)((char*)workspace + plan.dpre_bytes);
+  uint16_t* W1t = (uint16_t*)((char*)workspace + plan.dpre_bytes);                    // [d, h]
+  uint16_t* W2t = (uint16_t*)((char*)W1t + plan.wt_bytes / 2);                         // [h, d]
+  float* part = (float*)((char*)workspace + plan.dpre_bytes + plan.wt_bytes);
 
+  FP8MLP_TRY(launch_transpose_weights(W1, W2, d, h, W1t, W2t, st));
   // 1. dpost = dY W2 with the sqrt(post) epilogue -> dpre
   {
-    GemmArgs a{dY, d, W2, h, M, h, d, (int)cdiv(M, CfgDpost::BM), (int)cdiv(h, CfgDpost::BN), 1, d};
+    GemmArgs a{dY, d, W2t, d, M, h, d, (int)cdiv(M, CfgDpost::BM), (int)cdiv(h, CfgDpost::BN), 1, d};
     EpiDpre epi{post, dpre, h};
     FP8MLP_TRY(launch_gemm<CfgDpost, KID_DPOST>(a, epi, st));
   }
   // 2. dX = dpre W1
   {
-    GemmArgs a{dpre, h, W1, d, M, d, h, (int)cdiv(M, CfgDx::BM), (int)cdiv(d, CfgDx::BN), 1, h};
+    GemmArgs a{dpre, h, W1t, h, M, d, h, (int)cdiv(M, CfgDx::BM), (int)cdiv(d, CfgDx::BN), 1, h};
     EpiBf16Out epi{dX, d, 0, nullptr, 0.0f, nullptr, nullptr};
     FP8MLP_TRY(launch_gemm<CfgDx, KID_DX>(a, epi, st));
   }

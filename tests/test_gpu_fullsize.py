@@ -128,3 +128,29 @@ def test_fp8_linear_full_size(fm, which):
     assert (Wt_o == Wt.cpu().numpy()).all()
     ref = F.bf16_to_f64(O.fp8_linear(Xb[rows], float(sx.item()), Wt_o, inv_o))
     assert rel_fro(F.bf16_to_f64(bits(Y)[rows]), ref) < 4e-3
+
+
+def test_bwd_ragged_mid_size(fm):
+    """M = 22983 (not a multiple of any tile height) at d=768, h=3072: rows
+    around tile boundaries and the ragged last row of dX, rows of dW1 and
+    columns of dW2 against the oracle; two backward calls give the same bits."""
+    M, d, h = 22983, 768, 3072
+    ins = synth.mlp_inputs(M, d, h, 9, with_dy=True)
+    case(f"ragged mid-size backward M={M} d={d} h={h}")
+    blk = fm.Relu2MLP(bf16_dev(ins["W1"]), bf16_dev(ins["W2"]), margin=2.0, amax_init=1.0)
+    X, dY = bf16_dev(ins["X"]), bf16_dev(ins["dY"])
+    blk.forward(X)
+    Y, post, post_q = blk.forward(X)
+    dX, dW1, dW2 = blk.backward(dY, X, post)
+    dX2, _, _ = blk.backward(dY, X, post)
+    torch.cuda.synchronize()
+    assert (bits(dX) == bits(dX2)).all()                       # deterministic
+    rows = np.array([0, 1, 191, 192, 255, 256, 21760, 22783, 22784, M - 200, M - 1])
+    post_f = F.bf16_to_f64(bits(post))
+    bs = O.mlp_bwd_sampled(ins["dY"], ins["X"], ins["W1"], ins["W2"], post_f, rows, [0, 2000], [5, h - 1])
+    dx = F.bf16_to_f64(bits(dX)[rows])
+    assert rel_fro(dx, bs["dX_rows"]) < 4e-3
+    for i in range(len(rows)):
+        assert rel_fro(dx[i], bs["dX_rows"][i]) < 1e-2, rows[i]
+    assert rel_fro(dW1.cpu().numpy()[[0, 2000]].astype(np.float64), bs["dW1_rows"]) < 4e-3
+    assert rel_fro(dW2.cpu().numpy()[:, [5, h - 1]].astype(np.float64), bs["dW2_cols"]) < 1e-4
