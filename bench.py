@@ -42,7 +42,9 @@ KID_NAMES = {1: "up_gemm_relu2_quant", 2: "down_gemm_e4m3", 3: "down_gemm_bf16_e
              5: "dx_gemm", 6: "dw1_gemm", 7: "dw2_gemm", 8: "fp8_linear_gemm"}
 OTHER_NAMES = {"k_max_final": "amax_final", "k_amax_partial": "amax_partial", "k_cast_transpose": "cast_transpose",
                "k_splitk_reduce": "splitk_reduce", "k_quantize": "quantize_e4m3", "k_fill_zero": "fill_zero",
-               "k_zero_scalar": "zero_scalar", "k_scale_from_amax": "scale_from_amax", "k_max_small": "amax_small"}
+               "k_zero_scalar": "zero_scalar", "k_scale_from_amax": "scale_from_amax", "k_amax_small": "amax_small",
+               "k_transpose_weights": "transpose_weights", "k_rmsnorm_fwd": "rmsnorm_fwd", "k_rmsnorm_bwd": "rmsnorm_bwd",
+               "k_add_bf16": "add_bf16", "k_sgd_bf16": "sgd_update_bf16"}
 
 
 def log(msg):

@@ -154,6 +154,32 @@ int launch_amax(int dtype, const void* x, int64_t n, float* out, void* workspace
   return launch_status();
 }
 
+// First phase of an amax whose consumer finishes the reduction itself:
+// writes |x| maxima as fp32 bit patterns to partial[0 .. *count) (one value
+// for small tensors, one per block otherwise).  partial needs
+// max(4, amax_ws_bytes(n)) bytes.
+int launch_amax_partials(int dtype, const void* x, int64_t n, uint32_t* partial, int* count, hipStream_t stream) {
+  if (n <= kAmaxSmall) {
+    *count = 1;
+    TraceScope trace("amax_small", stream);
+    if (dtype == FP8MLP_F32)
+      hipLaunchKernelGGL(k_amax_small<FP8MLP_F32>, dim3(1), dim3(256), 0, stream, x, n, (float*)partial);
+    else
+      hipLaunchKernelGGL(k_amax_small<FP8MLP_BF16>, dim3(1), dim3(256), 0, stream, x, n, (float*)partial);
+    return launch_status();
+  }
+  const int per = dtype == FP8MLP_F32 ? 4 : 8;
+  int64_t blocks = cdiv(cdiv(n, per), 256 * 4);
+  if (blocks > kAmaxBlocks) blocks = kAmaxBlocks;
+  *count = (int)blocks;
+  TraceScope trace("amax_partial", stream);
+  if (dtype == FP8MLP_F32)
+    hipLaunchKernelGGL(k_amax_partial<FP8MLP_F32>, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, partial);
+  else
+    hipLaunchKernelGGL(k_amax_partial<FP8MLP_BF16>, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, partial);
+  return launch_status();
+}
+
 // ------------------------------------------------------------------ scale
 __global__ void k_scale_from_amax(const float* amax, float margin, float* scale_out, float* inv_out) {
   const float s = scale_from_amax(*amax, margin);
@@ -166,10 +192,19 @@ __global__ void k_scale_from_amax(const float* amax, float margin, float* scale_
 // read from scale_in, or computed as 448 / amax (exact policy).
 __global__ void __launch_bounds__(256) k_cast_transpose(const uint16_t* __restrict__ W, int64_t N, int64_t K,
                                                         uint8_t* __restrict__ Wt, const float* scale_in,
-                                                        const float* amax_in, float* scale_out, float* inv_out,
-                                                        float* amax_out) {
+                                                        const uint32_t* amax_part, int npart, float* scale_out,
+                                                        float* inv_out, float* amax_out) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[64][80];  // [k][n]
-  const float s = scale_in ? *scale_in : scale_from_amax(*amax_in, 1.0f);
+  __shared__ uint32_t red[4];
+  // every block finishes the amax from the per-block maxima (a few hundred
+  // words) instead of waiting for a separate reduction launch
+  float amax = 0.0f;
+  if (amax_part) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < npart; i += 256) m = amax_part[i] > m ? amax_part[i] : m;
+    amax = __uint_as_float(block_max_u32(m, red));
+  }
+  const float s = scale_in ? *scale_in : scale_from_amax(amax, 1.0f);
   const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
 #pragma unroll
   for (int it = 0; it < 2; it++) {
@@ -197,7 +232,7 @@ __global__ void __launch_bounds__(256) k_cast_transpose(const uint16_t* __restri
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
     if (scale_out) *scale_out = s;
     if (inv_out) *inv_out = 1.0f / s;
-    if (amax_out) *amax_out = amax_in ? *amax_in : 0.0f;
+    if (amax_out) *amax_out = amax;
   }
 }
 
@@ -267,14 +302,15 @@ int fp8_cast_transpose(const uint16_t* W, int64_t N, int64_t K, uint8_t* Wt_q, c
   FP8MLP_REQUIRE(need == 0 || aligned16(workspace), FP8MLP_E_ALIGN);
   FP8MLP_TRY(check_device());
   hipStream_t st = (hipStream_t)stream;
-  float* amax_slot = nullptr;
+  uint32_t* part = nullptr;
+  int npart = 0;
   if (need_amax) {
-    amax_slot = (float*)workspace;
-    FP8MLP_TRY(launch_amax(FP8MLP_BF16, W, N * K, amax_slot, (char*)workspace + 256, workspace_bytes - 256, st));
+    part = N * K <= kAmaxSmall ? (uint32_t*)workspace : (uint32_t*)((char*)workspace + 256);
+    FP8MLP_TRY(launch_amax_partials(FP8MLP_BF16, W, N * K, part, &npart, st));
   }
   dim3 grid((unsigned)cdiv(K, 64), (unsigned)cdiv(N, 64));
   TraceScope trace("cast_transpose", st);
-  hipLaunchKernelGGL(k_cast_transpose, grid, dim3(256), 0, st, W, N, K, Wt_q, scale_in, (const float*)amax_slot,
+  hipLaunchKernelGGL(k_cast_transpose, grid, dim3(256), 0, st, W, N, K, Wt_q, scale_in, (const uint32_t*)part, npart,
                      scale_out, inv_scale_out, amax_out);
   return launch_status();
 }

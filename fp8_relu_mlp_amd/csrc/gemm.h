@@ -97,7 +97,32 @@ struct GemmArgs {
   int64_t k_per_split;  // multiple of BK
   int stagger;          // > 0: blocks of the second residency slot start ~stagger x 4 us late
   int group_m;          // tile rows per group of the tile order (set by launch_gemm)
+  // Optional side job for wave 0 of block 0 (red_in != nullptr): the
+  // maximum of red_n fp32 values >= +0 or NaN, given as bit patterns, ->
+  // *red_out, and, if red_scale_out is set, the scale of *red_amax_prev and
+  // red_margin -> *red_scale_out.  Finishes a partial-amax reduction without
+  // a launch of its own.
+  const uint32_t* red_in;
+  int64_t red_n;
+  float* red_out;
+  const float* red_amax_prev;
+  float red_margin;
+  float* red_scale_out;
 };
+
+__device__ __forceinline__ void side_amax(const GemmArgs& a, int wave, int lane) {
+  if (a.red_in == nullptr || blockIdx.x != 0 || wave != 0) return;
+  uint32_t m = 0;
+  for (int64_t i = lane; i < a.red_n; i += 64) {
+    const uint32_t v = a.red_in[i] & 0x7fffffffu;
+    m = v > m ? v : m;
+  }
+  m = wave_max_u32(m);
+  if (lane == 0) {
+    *a.red_out = __uint_as_float(m);
+    if (a.red_scale_out) *a.red_scale_out = scale_from_amax(*a.red_amax_prev, a.red_margin);
+  }
+}
 
 // Per-block tile coordinates handed to the epilogue.
 struct TileCtx {
@@ -429,6 +454,7 @@ __global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) 
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
+  side_amax(a, wave, lane);
 
   // With two blocks per CU, blocks that start together reach their
   // epilogues together and leave the matrix cores idle meanwhile.  Delaying
@@ -614,6 +640,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs a, Epi epi) {
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = wave >> 2, wm = (wave >> 1) & 1, wn = 2 * (wave & 1) + g;
+  side_amax(a, wave, lane);
 
   const TilePos t = tile_pos<C>(a);
   const int KT = t.KT;

@@ -74,16 +74,28 @@ int mlp_relu2_fwd(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t
     EpiRelu2Quant epi{post, train ? post_q : nullptr, partial, amax_prev, margin, h, (int)plan.tn};
     FP8MLP_TRY(launch_gemm<CfgUp, KID_UP>(a, epi, st));
   }
-  // 2. reduce the partial amax tensor; record the scale that was used
-  FP8MLP_TRY(launch_max_small(partial, plan.tm * plan.tn, amax_out, amax_prev, margin, train ? scale_out : nullptr,
-                              st));
-  // 3. down-projection
+  if (M == 0) {
+    // nothing to multiply: amax = 0 (and the scale that would have been used)
+    return launch_max_small(partial, 0, amax_out, amax_prev, margin, train ? scale_out : nullptr, st);
+  }
+  // 2. down-projection; its block 0 also reduces the partial amax tensor and
+  //    records the scale that was used
+  auto side = [&](GemmArgs& a) {
+    a.red_in = (const uint32_t*)partial;
+    a.red_n = plan.tm * plan.tn;
+    a.red_out = amax_out;
+    a.red_amax_prev = amax_prev;
+    a.red_margin = margin;
+    a.red_scale_out = train ? scale_out : nullptr;
+  };
   if (train) {
     GemmArgs a{post_q, h, W2t_q, d, M, d, h, (int)cdiv(M, CfgDown8::BM), (int)cdiv(d, CfgDown8::BN), 1, h};
+    side(a);
     EpiBf16Out epi{Y, d, 1, amax_prev, margin, nullptr, w2_inv_scale};
     FP8MLP_TRY(launch_gemm<CfgDown8, KID_DOWN8>(a, epi, st));
   } else {
     GemmArgs a{post, h, W2, h, M, d, h, (int)cdiv(M, CfgDownBf16::BM), (int)cdiv(d, CfgDownBf16::BN), 1, h};
+    side(a);
     EpiBf16Out epi{Y, d, 0, nullptr, 0.0f, nullptr, nullptr};
     FP8MLP_TRY(launch_gemm<CfgDownBf16, KID_DOWN_BF16>(a, epi, st));
   }
