@@ -44,7 +44,7 @@ OTHER_NAMES = {"k_max_final": "amax_final", "k_amax_partial": "amax_partial", "k
                "k_splitk_reduce": "splitk_reduce", "k_quantize": "quantize_e4m3", "k_fill_zero": "fill_zero",
                "k_zero_scalar": "zero_scalar", "k_scale_from_amax": "scale_from_amax", "k_amax_small": "amax_small",
                "k_transpose_weights": "transpose_weights", "k_rmsnorm_fwd": "rmsnorm_fwd", "k_rmsnorm_bwd": "rmsnorm_bwd",
-               "k_add_bf16": "add_bf16", "k_sgd_bf16": "sgd_update_bf16"}
+               "k_add_bf16": "add_bf16", "k_sgd_bf16": "sgd_update_bf16", "k_mfma_probe": "mfma_probe"}
 
 
 def log(msg):
@@ -105,7 +105,7 @@ def summarize_profiles(outdir):
         with open(files[0]) as fh:
             return list(csv.DictReader(fh))
 
-    cmd_bench = "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extras"
+    cmd_bench = "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-extras"
     # kernel trace: per-dispatch durations
     trace = rows("kt", "*kernel_trace.csv")
     dur = {}
@@ -327,6 +327,27 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic.get(dom),
                 "algorithmic_flops_per_launch": fl, "algorithmic_bytes_per_launch": by}
 
+    # matrix-core rate on the workload's own operands (the clock under a dense
+    # MFMA load depends on the data; the published peaks assume 2.4 GHz)
+    log("matrix-core rate probe")
+    sink = torch.empty(fm.PROBE_BLOCKS * 256, dtype=torch.float32, device=dev)
+
+    def probe_rate(dtype, a, b, iters=20000):
+        fm.mfma_probe(dtype, a, b, iters // 10, sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fl = fm.mfma_probe(dtype, a, b, iters, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        return fl / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+    probe = {"bf16_tflops": round(probe_rate(fm.MFMA_BF16, X, W1), 1),
+             "e4m3_tflops": round(probe_rate(fm.MFMA_E4M3, post_q, blk.W2t_q), 1),
+             "operands": "X and W1 (bf16), post_q and W2t_q (e4m3) of this workload"}
+    roofline["probe_peak"] = probe["bf16_tflops"] if peak == PEAK_BF16 else probe["e4m3_tflops"]
+    roofline["frac_of_probe_peak"] = round(achieved / roofline["probe_peak"], 4)
+
     extras = {}
     if not args.no_extras:
         log("extra measurements")
@@ -346,6 +367,7 @@ def main():
         "pct_mixed_mfma_peak": round(100.0 * floor_us / (ms * 1e3), 2),
         "mixed_mfma_floor_us": round(floor_us, 1),
         "roofline": roofline,
+        "mfma_probe": probe,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "extras": extras,

@@ -155,6 +155,22 @@ def sgd_update_bf16(W, dW, lr, stream=None):
     check("sgd_update_bf16", lib().sgd_update_bf16(_p(W), _p(dW), W.numel(), float(lr), _stream(stream)))
 
 
+PROBE_BLOCKS = 256
+MFMA_BF16, MFMA_E4M3 = 0, 1
+
+
+def mfma_probe(dtype, a, b, iters, sink, stream=None):
+    """Matrix-core rate probe on operands taken from tensors a and b (see
+    fp8mlp_mfma_probe); sink: fp32 [PROBE_BLOCKS * 256].  Returns the flop
+    count of the call."""
+    if sink.numel() < PROBE_BLOCKS * 256 or sink.dtype != torch.float32:
+        raise ValueError("sink must hold PROBE_BLOCKS * 256 fp32 values")
+    check("fp8mlp_mfma_probe", lib().fp8mlp_mfma_probe(
+        int(dtype), _p(a), a.numel() * a.element_size(), _p(b), b.numel() * b.element_size(), int(iters), _p(sink),
+        _stream(stream)))
+    return PROBE_BLOCKS * 4 * 16 * int(iters) * (32768 if dtype == MFMA_BF16 else 131072)
+
+
 class KernelTimer:
     """Context manager around the library's per-kernel timing events.
 

@@ -40,6 +40,7 @@ SIGNATURES = {
     "rmsnorm_bwd": (c_int, [vp, vp, vp, vp, vp, c_i64, c_i64, vp]),
     "add_bf16": (c_int, [vp, vp, vp, c_i64, vp]),
     "sgd_update_bf16": (c_int, [vp, vp, c_i64, c_float, vp]),
+    "fp8mlp_mfma_probe": (c_int, [c_int, vp, c_i64, vp, c_i64, c_i64, vp, vp]),
     "fp8mlp_timing_start": (c_int, [c_int]),
     "fp8mlp_timing_stop": (c_int, []),
     "fp8mlp_timing_get": (c_int, [c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(c_float)]),

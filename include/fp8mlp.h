@@ -222,6 +222,27 @@ int add_bf16(const uint16_t* a, const uint16_t* b, uint16_t* out, int64_t n, voi
 int sgd_update_bf16(uint16_t* W, const float* dW, int64_t n, float lr, void* stream);
 
 /* ------------------------------------------------------------------------
+ * fp8mlp_mfma_probe -- matrix-core rate probe (a measurement aid, not part of
+ * the method).  The published MI355X peaks assume the boost clock; under a
+ * dense MFMA load the clock falls with the switching activity of the
+ * operands, so the benchmark measures the rate the chip sustains on its own
+ * data.  Launches FP8MLP_PROBE_BLOCKS blocks of 4 waves; every wave loads 4 + 4
+ * operand fragments from a and b (read modulo a_bytes / b_bytes) and issues
+ * iters rounds of 16 independent 32x32 MFMAs:
+ *   FP8MLP_MFMA_BF16: v_mfma_f32_32x32x16_bf16, 32768 flop each;
+ *   FP8MLP_MFMA_E4M3: v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3, unit scales),
+ *                     131072 flop each.
+ * Flop per call = FP8MLP_PROBE_BLOCKS * 4 * 16 * iters * (flop per MFMA).
+ * sink: device fp32 [FP8MLP_PROBE_BLOCKS * 256], overwritten.  a, b: device,
+ * 16-byte aligned, at least 16 bytes.  1 <= iters <= 2^24.
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_ARCH, E_ARG, E_HIP.
+ * ---------------------------------------------------------------------- */
+enum { FP8MLP_MFMA_BF16 = 0, FP8MLP_MFMA_E4M3 = 1 };
+#define FP8MLP_PROBE_BLOCKS 256
+int fp8mlp_mfma_probe(int dtype, const void* a, int64_t a_bytes, const void* b, int64_t b_bytes, int64_t iters,
+                      float* sink, void* stream);
+
+/* ------------------------------------------------------------------------
  * Per-kernel timing (benchmarking / profiling aid, not part of the method).
  * fp8mlp_timing_start(capacity) creates up to `capacity` hipEvent pairs
  * (driver objects, no device memory) and, until fp8mlp_timing_stop(), brackets

@@ -124,3 +124,21 @@ def test_cast_transpose_w2_matches_generic(fm):
     assert (out.cpu().numpy() == ref).all()
     assert (f32_bits(s.item()), f32_bits(inv.item()), f32_bits(am.item())) == \
         (f32_bits(rs), f32_bits(rinv), f32_bits(ra))
+
+
+def test_mfma_probe_runs():
+    """The matrix-core rate probe runs on bf16 and e4m3 operands and writes its
+    sink (a measurement aid; its flop count is what the benchmark divides)."""
+    import fp8_relu_mlp_amd as fm
+    case("mfma probe")
+    a = torch.randn(1 << 16, device=DEV).to(torch.bfloat16)
+    b = torch.randn(1 << 16, device=DEV).to(torch.bfloat16)
+    sink = torch.zeros(fm.PROBE_BLOCKS * 256, dtype=torch.float32, device=DEV)
+    assert fm.mfma_probe(fm.MFMA_BF16, a, b, 10, sink) == fm.PROBE_BLOCKS * 4 * 16 * 10 * 32768
+    torch.cuda.synchronize()
+    assert (sink != 0).any()
+    q = torch.randint(0, 0x77, (1 << 16,), dtype=torch.uint8, device=DEV)
+    sink.zero_()
+    assert fm.mfma_probe(fm.MFMA_E4M3, q, q, 10, sink) == fm.PROBE_BLOCKS * 4 * 16 * 10 * 131072
+    torch.cuda.synchronize()
+    assert torch.isfinite(sink).all()
