@@ -176,6 +176,43 @@ def mlp_fwd(X_bits, W1_bits, W2t_codes, w2_inv_scale, amax_prev, margin,
     return out
 
 
+def up_relu2_fp8(X_bits, x_scale, W1t_codes, w1_inv_scale, rnd=bf16):
+    """post = relu(pre)^2 with the up-projection in e4m3 as well.
+
+    [S] "From Unoptimized", "Approach" item 5: both MLP GEMMs run in e4m3 on
+    the training forward.  The pages do not say how X is scaled; reading: a
+    per-tensor multiplier sx supplied by the caller, as for the attention
+    projections ([S] item 1), with W1 held transposed in e4m3 like W2:
+      Xq  = e4m3(fl32(X * sx))
+      acc = dec(Xq) dec(W1t)        (exact in float64, as in ``down_fp8``)
+      pre = acc * fl32(1/sx) * w1_inv_scale
+      post = rnd(relu(pre)^2)
+    Returns (post, Xq codes, pre), post rounded by ``rnd``, pre unrounded.
+    """
+    X = bf16_to_f64(X_bits)
+    sx = float(np.float32(x_scale))
+    xq = e4m3_encode(fl32(X * sx))
+    acc = e4m3_decode(xq) @ e4m3_decode(W1t_codes)
+    pre = acc * inv_scale(sx) * float(np.float32(w1_inv_scale))
+    r = np.maximum(pre, 0.0)
+    return rnd(r * r), xq, pre
+
+
+def mlp_fwd_fp8up(X_bits, x_scale, W1t_codes, w1_inv_scale, W2t_codes, w2_inv_scale, amax_prev, margin,
+                  post_bits=None):
+    """The training forward with both GEMMs in e4m3 ([S] "Approach" item 5):
+    ``up_relu2_fp8``, then the same delayed-scale quantisation, partial amax
+    and FP8 down-projection as ``mlp_fwd`` in train mode.  ``post_bits``
+    lets a test feed the GPU's own bf16 post to the later steps."""
+    xq = None
+    if post_bits is None:
+        post, xq, _ = up_relu2_fp8(X_bits, x_scale, W1t_codes, w1_inv_scale)
+        post_bits = bf16_round(post)
+    out = mlp_fwd(X_bits, None, W2t_codes, w2_inv_scale, amax_prev, margin, post_bits=post_bits)
+    out.update(xq=xq, x_amax=amax(bf16_to_f64(X_bits)))
+    return out
+
+
 # --------------------------------------------------------------------------
 # backward (bf16 path, straight through the fp8 forward)
 # --------------------------------------------------------------------------

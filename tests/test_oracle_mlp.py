@@ -283,3 +283,90 @@ def test_fp8_linear_matches_loops_and_torch():
         for n in range(N):
             acc = sum(xq[m, k] * wd[k, n] for k in range(K))
             assert Y[m, n] == F.bf16(acc * inv_sx * inv_sw)
+
+
+# ------------------------------------------------------------------ FP8 up-projection
+def _pow2_case(M=20, d=32, h=48, seed=11):
+    # X = a/4 and W1 = b/8 with small integers |a|, |b| <= 7, and one W1
+    # entry at exactly 7/8: the W1 scale is 448 / (7/8) = 512 = 2^9 and X is
+    # scaled by 16, so X*16 = 4a and W1*512 = 64b are e4m3 values (<= 3
+    # significant bits, <= 448) and both quantisations are exact.
+    g = np.random.default_rng(seed)
+    X = g.integers(-7, 8, size=(M, d)) / 4.0
+    W1 = g.integers(-7, 8, size=(h, d)) / 8.0
+    W1[0, 0] = 7 / 8
+    W1[np.abs(W1) > 7 / 8] = 0.5
+    return _bf16_bits(X), _bf16_bits(W1)
+
+
+def test_fp8_up_lossless_power_of_two_scales():
+    X, W1 = _pow2_case()
+    W1t, s1, inv1, a1 = O.cast_transpose(W1)
+    assert (a1, s1, inv1) == (7 / 8, 512.0, 2.0 ** -9)
+    post, xq, pre = O.up_relu2_fp8(X, 16.0, W1t, inv1, rnd=O.exact)
+    Xf, W1f = F.bf16_to_f64(X), F.bf16_to_f64(W1)
+    assert (F.e4m3_decode(xq) == Xf * 16).all()
+    assert (pre == Xf @ W1f.T).all()               # exact, not approximately
+    assert (post == np.maximum(Xf @ W1f.T, 0) ** 2).all()
+    # the rounded post equals the bf16 up-projection's
+    post_r, _, _ = O.up_relu2_fp8(X, 16.0, W1t, inv1)
+    assert (post_r == O.up_relu2(X, W1)).all()
+
+
+def test_fp8_up_matches_loops_and_torch_cast():
+    """Quantise X and W1 with torch's own float8_e4m3fn cast (independent of
+    the oracle's encoder), multiply in explicit loops over the untransposed
+    W1 (which pins the orientation of the transposed cache) and dequantise."""
+    M, d, h = 5, 32, 12
+    ins = synth.mlp_inputs(M, d, h, 23)
+    W1t, s1, inv1, _ = O.cast_transpose(ins["W1"])
+    Xf, W1f = F.bf16_to_f64(ins["X"]), F.bf16_to_f64(ins["W1"])
+    sx = O.exact_scale(O.amax(Xf))
+    post, xq, pre = O.up_relu2_fp8(ins["X"], sx, W1t, inv1)
+
+    def cast(v):
+        return torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+    xd, wd = cast(Xf * sx), cast(W1f * s1)
+    assert (F.e4m3_decode(xq) == xd).all()
+    inv_sx = float(np.float32(1.0 / np.float32(sx)))
+    for m in range(M):
+        for n in range(h):
+            acc = sum(Fraction(float(xd[m, k])) * Fraction(float(wd[n, k])) for k in range(d))
+            p = float(acc) * inv_sx * inv1
+            assert pre[m, n] == p
+            assert post[m, n] == F.bf16(max(p, 0.0) ** 2)
+
+
+def test_fp8_up_close_to_exact_function():
+    """e4m3 keeps 4 significant bits (relative step <= 2^-4 per operand), so
+    the fp8 pre stays within a few per cent of X W1^T; a dropped or doubled
+    dequantisation factor would be off by the scales (>= 2^5 here)."""
+    M, d, h = 64, 256, 384
+    ins = synth.mlp_inputs(M, d, h, 24)
+    W1t, _, inv1, _ = O.cast_transpose(ins["W1"])
+    Xf = F.bf16_to_f64(ins["X"])
+    sx = O.exact_scale(O.amax(Xf))
+    post, _, pre = O.up_relu2_fp8(ins["X"], sx, W1t, inv1)
+    exact_pre = Xf @ F.bf16_to_f64(ins["W1"]).T
+    e_pre = np.linalg.norm(pre - exact_pre) / np.linalg.norm(exact_pre)
+    assert 1e-3 < e_pre < 0.08
+    e_post = np.linalg.norm(post - O.up_relu2(ins["X"], ins["W1"])) / np.linalg.norm(post)
+    assert e_post < 0.15
+
+
+def test_fp8_up_forward_composes_like_train_forward():
+    M, d, h = 16, 64, 128
+    ins = synth.mlp_inputs(M, d, h, 25)
+    W1t, _, inv1, _ = O.cast_transpose(ins["W1"])
+    W2t, _, inv2, _ = O.cast_transpose(ins["W2"])
+    Xf = F.bf16_to_f64(ins["X"])
+    sx = O.exact_scale(O.amax(Xf))
+    out = O.mlp_fwd_fp8up(ins["X"], sx, W1t, inv1, W2t, inv2, 3.0, 2.0)
+    assert out["x_amax"] == np.abs(Xf).max()
+    post, xq, _ = O.up_relu2_fp8(ins["X"], sx, W1t, inv1)
+    assert (out["xq"] == xq).all() and (F.bf16_to_f64(out["post"]) == post).all()
+    ref = O.mlp_fwd(ins["X"], ins["W1"], W2t, inv2, 3.0, 2.0, post_bits=out["post"])
+    for k in ("post_q", "y"):
+        assert (out[k] == ref[k]).all()
+    assert out["scale"] == ref["scale"] == O.delayed_scale(3.0, 2.0)
