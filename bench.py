@@ -39,7 +39,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "hbm_traffic_mlp_fwd_bwd_M49152.txt")
 # GEMM kernels carry the launch site as their last template argument
 KID_NAMES = {1: "up_gemm_relu2_quant", 2: "down_gemm_e4m3", 3: "down_gemm_bf16_eval", 4: "dpost_gemm_dpre",
-             5: "dx_gemm", 6: "dw1_gemm", 7: "dw2_gemm", 8: "fp8_linear_gemm"}
+             5: "dx_gemm", 6: "dw1_gemm", 7: "dw2_gemm", 8: "fp8_linear_gemm", 9: "up_gemm_e4m3_relu2_quant"}
 OTHER_NAMES = {"k_max_final": "amax_final", "k_amax_partial": "amax_partial", "k_cast_transpose": "cast_transpose",
                "k_splitk_reduce": "splitk_reduce", "k_quantize": "quantize_e4m3", "k_fill_zero": "fill_zero",
                "k_zero_scalar": "zero_scalar", "k_scale_from_amax": "scale_from_amax", "k_amax_small": "amax_small",
@@ -63,12 +63,15 @@ def kernel_work(M, d, h):
         "dw1_gemm": (mdh2, M * h * b16 + M * d * b16 + h * d * f32, PEAK_BF16),
         "dw2_gemm": (mdh2, M * d * b16 + M * h * b16 + d * h * f32, PEAK_BF16),
         "down_gemm_bf16_eval": (mdh2, M * h * b16 + h * d * b16 + M * d * b16, PEAK_BF16),
+        "up_gemm_e4m3_relu2_quant": (mdh2, M * d * b8 + h * d * b8 + M * h * (b16 + b8), PEAK_FP8),
     }
 
 
-def mixed_floor_us(M, d, h):
+def mixed_floor_us(M, d, h, fp8_gemms=1):
+    """Time of the six GEMMs of a step at the published peaks, `fp8_gemms` of
+    them (the down-projection; with the e4m3 up-projection two) in e4m3."""
     mdh = float(M) * d * h
-    return (10 * mdh / (PEAK_BF16 * 1e12) + 2 * mdh / (PEAK_FP8 * 1e12)) * 1e6
+    return ((12 - 2 * fp8_gemms) * mdh / (PEAK_BF16 * 1e12) + 2 * fp8_gemms * mdh / (PEAK_FP8 * 1e12)) * 1e6
 
 
 def kernel_source_hash():
@@ -351,7 +354,8 @@ def main():
     extras = {}
     if not args.no_extras:
         log("extra measurements")
-        extras = extra_measurements(fm, torch, dev, X, W2, blk, post, post_q, Y, ws_f)
+        extras = extra_measurements(fm, torch, dev, X, W1, W2, dY, blk, post, post_q, Y, dX, dW1, dW2, ws_f, ws_b,
+                                    ws_c)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -375,9 +379,12 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def extra_measurements(fm, torch, dev, X, W2, blk, post, post_q, Y, ws_f, reps=20):
+def extra_measurements(fm, torch, dev, X, W1, W2, dY, blk, post, post_q, Y, dX, dW1, dW2, ws_f, ws_b, ws_c,
+                       reps=20):
     """Side measurements (not part of `value`): forward-only TRAIN vs EVAL
-    (bf16 down-projection ablation), the W2 cache refresh, the layer-stack
+    (bf16 down-projection ablation), the W2 cache refresh, the step with the
+    up-projection in e4m3 as well (mlp_relu2_fwd_fp8up, both weight caches
+    refreshed after the update), the layer-stack
     workload (12 layers x 8 SGD steps at M=65536, with the share of post
     values the e4m3 copy clipped per layer and step) and the FP8 attention
     projections."""
@@ -408,6 +415,38 @@ def extra_measurements(fm, torch, dev, X, W2, blk, post, post_q, Y, ws_f, reps=2
                                                   workspace=ws_c))
     out["w2_refresh_us"] = round(t_w2 * 1e3, 2)
     out["w2_refresh_gbs_alg"] = round((D * H * 2 * 2 + D * H) / (t_w2 * 1e-3) / 1e9, 1)
+
+    # the same step with both forward GEMMs in e4m3
+    blk8 = fm.Relu2MLP(W1, W2, margin=MARGIN, amax_init=1.0, fp8_up=True)
+    ws_8 = torch.empty(max(1, fm.lib().mlp_relu2_fwd_fp8up_workspace(M, D, H)), dtype=torch.uint8, device=dev)
+    blk8.forward(X, post=post, post_q=post_q, Y=Y, workspace=ws_8)        # bootstrap both amaxes
+
+    def step8():
+        blk8.forward(X, post=post, post_q=post_q, Y=Y, workspace=ws_8)
+        blk8.backward(dY, X, post, dX, dW1, dW2, workspace=ws_b)
+        blk8.refresh_caches(workspace=ws_c)
+
+    t_f8 = timed(lambda: blk8.forward(X, post=post, post_q=post_q, Y=Y, carry=False, workspace=ws_8))
+    t_s8 = timed(step8)
+    out["fp8up_fwd_ms"] = round(t_f8, 4)
+    out["fp8up_fwd_tflops"] = round(2 * mdh2 / (t_f8 * 1e-3) / 1e12, 1)
+    out["fp8up_step_ms"] = round(t_s8, 4)
+    out["fp8up_step_tflops"] = round(6 * mdh2 / (t_s8 * 1e-3) / 1e12, 1)
+    out["fp8up_step_pct_mixed_mfma_peak"] = round(100.0 * mixed_floor_us(M, D, H, 2) / (t_s8 * 1e3), 2)
+    with fm.KernelTimer(64 * reps) as kt:
+        for _ in range(reps):
+            step8()
+    torch.cuda.synchronize()
+    ts = [t for name, t in kt.records() if name == "up_gemm_e4m3_relu2_quant"]
+    if ts:
+        us = 1e3 * sum(ts) / len(ts)
+        out["fp8up_up_gemm_us"] = round(us, 2)
+        out["fp8up_up_gemm_tflops"] = round(mdh2 / (us * 1e-6) / 1e12, 1)
+        out["fp8up_up_gemm_frac_fp8_peak"] = round(mdh2 / (us * 1e-6) / 1e12 / PEAK_FP8, 4)
+    xq = [t for name, t in kt.records() if name == "quantize_e4m3"]
+    if xq:
+        out["fp8up_quantize_x_us"] = round(1e3 * sum(xq) / len(xq), 2)
+    del blk8, ws_8
 
     # layer-stack workload: 12 layers x 8 SGD steps at M=65536 (state carry per layer)
     from fp8_relu_mlp_amd.stack import Relu2Stack

@@ -7,7 +7,7 @@ PyTorch supplies device memory and streams and nothing else.  If the library
 is not built, the first call raises.
 
 Entry points (same names as the C ABI):
-  mlp_relu2_fwd, mlp_relu2_bwd, fp8_cast_transpose, fp8_cast_transpose_w2,
+  mlp_relu2_fwd, mlp_relu2_fwd_fp8up, mlp_relu2_bwd, fp8_cast_transpose, fp8_cast_transpose_w2,
   amax_reduce, fp8_scale_from_amax, fp8_linear, and the layer-stack helpers
   rmsnorm_fwd, rmsnorm_bwd, add_bf16, sgd_update_bf16
 and ``Relu2MLP``, one MLP block's device state (bf16 weights, the transposed
@@ -23,7 +23,7 @@ EVAL_BF16 = 1
 F32 = 0
 BF16 = 1
 
-__all__ = ["mlp_relu2_fwd", "mlp_relu2_bwd", "fp8_cast_transpose", "fp8_cast_transpose_w2", "amax_reduce",
+__all__ = ["mlp_relu2_fwd", "mlp_relu2_fwd_fp8up", "mlp_relu2_bwd", "fp8_cast_transpose", "fp8_cast_transpose_w2", "amax_reduce",
            "fp8_scale_from_amax", "fp8_linear", "rmsnorm_fwd", "rmsnorm_bwd", "add_bf16", "sgd_update_bf16",
            "Relu2MLP", "KernelTimer", "Fp8MlpError", "TRAIN_FP8", "EVAL_BF16"]
 
@@ -64,6 +64,21 @@ def mlp_relu2_fwd(mode, X, W1, W2t_q, w2_inv_scale, W2, amax_prev, margin, post,
     check("mlp_relu2_fwd", L.mlp_relu2_fwd(
         mode, _p(X), _p(W1), _p(W2t_q), _p(w2_inv_scale), _p(W2), _p(amax_prev), float(margin), _p(post),
         _p(post_q), _p(amax_out), _p(scale_out), _p(Y), M, d, h, _p(ws), wsb, _stream(stream)))
+
+
+def mlp_relu2_fwd_fp8up(X, x_scale, W1t_q, w1_inv_scale, W2t_q, w2_inv_scale, amax_prev, margin, post, post_q,
+                        amax_out, scale_out, Y, x_amax_out=None, workspace=None, stream=None):
+    """See mlp_relu2_fwd_fp8up in include/fp8mlp.h: the training forward with
+    both GEMMs in e4m3.  X [M,d] bf16, W1t_q [d,h] uint8 (fp8_cast_transpose of
+    W1), W2t_q [h,d] uint8; scalars are 1-element fp32 device tensors."""
+    M, d = X.shape
+    h = W1t_q.shape[1]
+    L = lib()
+    ws, wsb = _ws(L.mlp_relu2_fwd_fp8up_workspace(M, d, h), workspace, X.device)
+    check("mlp_relu2_fwd_fp8up", L.mlp_relu2_fwd_fp8up(
+        _p(X), _p(x_scale), _p(W1t_q), _p(w1_inv_scale), _p(W2t_q), _p(w2_inv_scale), _p(amax_prev),
+        float(margin), _p(post), _p(post_q), _p(amax_out), _p(scale_out), _p(Y), _p(x_amax_out), M, d, h,
+        _p(ws), wsb, _stream(stream)))
 
 
 def mlp_relu2_bwd(dY, X, W1, W2, post, dX, dW1, dW2, accumulate=False, workspace=None, stream=None):
@@ -216,9 +231,15 @@ class Relu2MLP:
     of the previous step (``amax_prev``), which the next forward turns into
     its quantisation scale.  Carrying the state is a buffer swap: the amax a
     forward writes becomes the next forward's ``amax_prev``.
+
+    With ``fp8_up`` the training forward runs the up-projection in e4m3 too
+    (mlp_relu2_fwd_fp8up): the block then also keeps the transposed e4m3 W1
+    cache W1t_q [d,h] (``refresh_caches`` renews both caches) and the amax of
+    its input X from the previous step (``x_amax_prev``), from which each
+    forward derives the input's scale with the same margin.
     """
 
-    def __init__(self, W1, W2, margin=2.0, amax_init=None):
+    def __init__(self, W1, W2, margin=2.0, amax_init=None, fp8_up=False, x_amax_init=None):
         dev = W1.device
         self.W1, self.W2, self.margin = W1, W2, float(margin)
         h, d = W1.shape
@@ -229,24 +250,47 @@ class Relu2MLP:
         self.amax_prev, self._amax_next, self.scale_used = f(), f(), f()
         if amax_init is not None:
             self.amax_prev.fill_(float(amax_init))
-        self.refresh_w2_cache()
+        self.fp8_up = bool(fp8_up)
+        if self.fp8_up:
+            self.w1_scale, self.w1_inv_scale, self.w1_amax = f(), f(), f()
+            self.W1t_q = torch.empty((d, h), dtype=torch.uint8, device=dev)
+            self.x_amax_prev, self._x_amax_next, self.x_scale = f(), f(), f()
+            if x_amax_init is not None:
+                self.x_amax_prev.fill_(float(x_amax_init))
+        self.refresh_caches()
 
     def refresh_w2_cache(self, workspace=None, stream=None):
         fp8_cast_transpose_w2(self.W2, self.W2t_q, self.w2_scale, self.w2_inv_scale, self.w2_amax,
                               workspace=workspace, stream=stream)
 
+    def refresh_caches(self, workspace=None, stream=None):
+        """Renew the e4m3 weight caches after an update of W2 (and of W1 with fp8_up)."""
+        self.refresh_w2_cache(workspace=workspace, stream=stream)
+        if self.fp8_up:
+            fp8_cast_transpose(self.W1, self.W1t_q, None, self.w1_scale, self.w1_inv_scale, self.w1_amax,
+                               workspace=workspace, stream=stream)
+
     def forward(self, X, mode=TRAIN_FP8, post=None, post_q=None, Y=None, carry=True, workspace=None, stream=None):
         """Returns (Y, post, post_q).  With carry, the amax measured here
-        becomes amax_prev for the next call."""
+        becomes amax_prev for the next call (and, with fp8_up, max |X| becomes
+        x_amax_prev)."""
         M = X.shape[0]
         dev = X.device
         post = torch.empty((M, self.h), dtype=torch.bfloat16, device=dev) if post is None else post
         if mode == TRAIN_FP8 and post_q is None:
             post_q = torch.empty((M, self.h), dtype=torch.uint8, device=dev)
         Y = torch.empty((M, self.d), dtype=torch.bfloat16, device=dev) if Y is None else Y
-        mlp_relu2_fwd(mode, X, self.W1, self.W2t_q, self.w2_inv_scale, self.W2, self.amax_prev, self.margin,
-                      post, post_q if mode == TRAIN_FP8 else None, self._amax_next,
-                      self.scale_used if mode == TRAIN_FP8 else None, Y, workspace=workspace, stream=stream)
+        if mode == TRAIN_FP8 and self.fp8_up:
+            fp8_scale_from_amax(self.x_amax_prev, self.margin, self.x_scale, stream=stream)
+            mlp_relu2_fwd_fp8up(X, self.x_scale, self.W1t_q, self.w1_inv_scale, self.W2t_q, self.w2_inv_scale,
+                                self.amax_prev, self.margin, post, post_q, self._amax_next, self.scale_used, Y,
+                                x_amax_out=self._x_amax_next, workspace=workspace, stream=stream)
+            if carry:
+                self.x_amax_prev, self._x_amax_next = self._x_amax_next, self.x_amax_prev
+        else:
+            mlp_relu2_fwd(mode, X, self.W1, self.W2t_q, self.w2_inv_scale, self.W2, self.amax_prev, self.margin,
+                          post, post_q if mode == TRAIN_FP8 else None, self._amax_next,
+                          self.scale_used if mode == TRAIN_FP8 else None, Y, workspace=workspace, stream=stream)
         if carry:
             self.amax_prev, self._amax_next = self._amax_next, self.amax_prev
         return Y, post, post_q

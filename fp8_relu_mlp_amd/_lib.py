@@ -26,6 +26,9 @@ SIGNATURES = {
     "mlp_relu2_fwd_workspace": (c_size, [c_i64, c_i64, c_i64]),
     "mlp_relu2_fwd": (c_int, [c_int, vp, vp, vp, vp, vp, vp, c_float, vp, vp, vp, vp, vp,
                               c_i64, c_i64, c_i64, vp, c_size, vp]),
+    "mlp_relu2_fwd_fp8up_workspace": (c_size, [c_i64, c_i64, c_i64]),
+    "mlp_relu2_fwd_fp8up": (c_int, [vp, vp, vp, vp, vp, vp, vp, c_float, vp, vp, vp, vp, vp, vp,
+                                    c_i64, c_i64, c_i64, vp, c_size, vp]),
     "mlp_relu2_bwd_workspace": (c_size, [c_i64, c_i64, c_i64]),
     "mlp_relu2_bwd": (c_int, [vp, vp, vp, vp, vp, vp, vp, vp, c_int, c_i64, c_i64, c_i64, vp, c_size, vp]),
     "fp8_cast_transpose_workspace": (c_size, [c_i64, c_i64]),

@@ -119,7 +119,10 @@ __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
 // post is >= +0 or NaN, so its bf16 bit patterns order like the values (NaN
 // above +inf): the tile maximum is a max of 16-bit patterns and a NaN reaches
 // amax.  The e4m3 copy is made from the staged bf16 values on the way out.
-struct EpiRelu2Quant {
+// With DEQ (the up-projection itself in e4m3), the accumulators are first
+// dequantised: pre = fp32(fp32(acc * fp32(1 / *x_scale)) * *w_inv).
+template <bool DEQ>
+struct EpiRelu2QuantT {
   uint16_t* post;
   uint8_t* post_q;        // nullptr: no quantised copy (eval)
   float* partial;         // [tiles_m * tiles_n]
@@ -127,15 +130,24 @@ struct EpiRelu2Quant {
   float margin;
   int64_t ld;             // h
   int tiles_n;
+  const float* x_scale = nullptr;   // DEQ only
+  const float* w_inv = nullptr;     // DEQ only
 
   template <class C>
   static constexpr int lds_bytes() { return Tile16<C>::BYTES + 4 * C::NW; }
 
   template <class C>
   __device__ __forceinline__ void run(const TileCtx& c, f32x16 (&acc)[C::FM][C::FN], FP8MLP_LDS char* smem) {
-    static_assert(C::PERM, "needs 16 consecutive columns per lane");
+    // Without PERM (transposed e4m3 reads of the second operand) a lane holds
+    // four runs of four columns of a 32-column fragment; h is a multiple of
+    // 32, so a fragment is wholly inside or outside the matrix either way.
     using T = Tile16<C>;
     const float s = post_q ? scale_from_amax(*amax_prev, margin) : 1.0f;
+    float dq_x = 1.0f, dq_w = 1.0f;
+    if constexpr (DEQ) {
+      dq_x = 1.0f / *x_scale;
+      dq_w = *w_inv;
+    }
     uint32_t mx = 0;   // two running 16-bit maxima
     const bool interior = c.m0 + C::BM <= c.M && c.n0 + C::BN <= c.N;
     __syncthreads();   // every wave is done with the last pipeline stage
@@ -149,8 +161,14 @@ struct EpiRelu2Quant {
         for (int fn = 0; fn < C::FN; fn++) {
           uint32_t pk[8];
 #pragma unroll
-          for (int e = 0; e < 16; e += 2)
-            pk[e / 2] = opaque(pack_bf16x2(relu_sq(acc[fm][fn][e]), relu_sq(acc[fm][fn][e + 1])));
+          for (int e = 0; e < 16; e += 2) {
+            float v0 = acc[fm][fn][e], v1 = acc[fm][fn][e + 1];
+            if constexpr (DEQ) {
+              v0 = (v0 * dq_x) * dq_w;
+              v1 = (v1 * dq_x) * dq_w;
+            }
+            pk[e / 2] = opaque(pack_bf16x2(relu_sq(v0), relu_sq(v1)));
+          }
           if (!EDGE || (row_in && c.n0 + T::frag_chunk(c, fn) * 8 < c.N)) {
 #pragma unroll
             for (int i = 0; i < 8; i++) mx = max_u16x2(mx, pk[i]);
@@ -220,6 +238,7 @@ struct EpiRelu2Quant {
     if (threadIdx.x == 0) partial[c.tm * tiles_n + c.tn] = tile_max;
   }
 };
+using EpiRelu2Quant = EpiRelu2QuantT<false>;
 
 // bf16 output, optionally dequantised:
 //   mode 0: Y = bf16(acc)

@@ -60,5 +60,13 @@ int launch_max_small(const float* x, int64_t n, float* out, const float* amax_pr
 int launch_amax(int dtype, const void* x, int64_t n, float* out, void* workspace, size_t ws_bytes,
                 hipStream_t stream);
 size_t amax_ws_bytes(int64_t n);
+// Xq = e4m3(fp32(X * *scale)) over n elements (a multiple of 128) in at
+// most kQuantBlocks blocks (linear.hip).  When partial is given, block b
+// writes max |X| over its elements to partial[b]; *count receives the number
+// of blocks (0 for n = 0, which launches nothing).
+constexpr int kQuantBlocks = 4096;
+constexpr size_t quantize_partial_bytes() { return (size_t)kQuantBlocks * 4; }
+int launch_quantize(const uint16_t* X, int64_t n, const float* scale, uint8_t* Xq, uint32_t* partial,
+                    int64_t* count, hipStream_t stream);
 
 }  // namespace fp8mlp

@@ -29,6 +29,7 @@ inline const char* kid_name(int kid) {
     case KID_DW1: return "dw1_gemm";
     case KID_DW2: return "dw2_gemm";
     case KID_LINEAR: return "fp8_linear_gemm";
+    case KID_UP8: return "up_gemm_e4m3_relu2_quant";
   }
   return "gemm";
 }

@@ -15,13 +15,13 @@ namespace fp8mlp {
 // Xq [M,K] e4m3 . Wt_q [K,N] e4m3 (transposing LDS reads)
 using CfgLin = GemmCfg<1, 192, 128, 128, 2, 2, KC, MNC>;
 
-__global__ void k_zero_scalar(float* p) { *p = 0.0f; }
-
-// Xq = e4m3(fp32(X * s)); 16 elements per thread and step; amax_out, when
-// given, receives max |X| through an atomic max on bit patterns.
+// Xq = e4m3(fp32(X * s)); 16 elements per thread and step.  With `partial`,
+// block b also writes the maximum of |X| over the elements it converted to
+// partial[b] (fp32 bit pattern), for the consumer to finish the reduction.
 __global__ void __launch_bounds__(256) k_quantize(const uint16_t* __restrict__ X, int64_t n16,
                                                   const float* __restrict__ scale, uint8_t* __restrict__ Xq,
-                                                  float* amax_out) {
+                                                  uint32_t* __restrict__ partial) {
+  __shared__ uint32_t red[4];
   const float s = *scale;
   uint32_t mx = 0;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) {
@@ -39,10 +39,28 @@ __global__ void __launch_bounds__(256) k_quantize(const uint16_t* __restrict__ X
     }
     *((i32x4*)Xq + i) = q;
   }
-  if (amax_out) {
+  if (partial) {
     mx = wave_max_u32(mx);
-    if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)amax_out, mx);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t m01 = red[0] > red[1] ? red[0] : red[1], m23 = red[2] > red[3] ? red[2] : red[3];
+      partial[blockIdx.x] = m01 > m23 ? m01 : m23;
+    }
   }
+}
+
+int launch_quantize(const uint16_t* X, int64_t n, const float* scale, uint8_t* Xq, uint32_t* partial,
+                    int64_t* count, hipStream_t st) {
+  *count = 0;
+  if (n == 0) return FP8MLP_OK;
+  const int64_t n16 = n / 16;
+  int64_t blocks = cdiv(n16, 256 * 4);
+  if (blocks > kQuantBlocks) blocks = kQuantBlocks;
+  TraceScope trace("quantize_e4m3", st);
+  hipLaunchKernelGGL(k_quantize, dim3((unsigned)blocks), dim3(256), 0, st, X, n16, scale, Xq, partial);
+  *count = blocks;
+  return launch_status();
 }
 
 }  // namespace fp8mlp
@@ -53,7 +71,7 @@ extern "C" {
 
 size_t fp8_linear_workspace(int64_t M, int64_t K) {
   if (M <= 0 || K <= 0) return 0;
-  return align_up((size_t)(M * K), 256);
+  return align_up((size_t)(M * K), 256) + quantize_partial_bytes();
 }
 
 int fp8_linear(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, const float* w_inv_scale,
@@ -71,22 +89,21 @@ int fp8_linear(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, con
   FP8MLP_REQUIRE(need == 0 || aligned16(workspace), FP8MLP_E_ALIGN);
   FP8MLP_TRY(check_device());
   hipStream_t st = (hipStream_t)stream;
-  if (x_amax_out) {
-    TraceScope trace("zero_scalar", st);
-    hipLaunchKernelGGL(k_zero_scalar, dim3(1), dim3(1), 0, st, x_amax_out);
-    FP8MLP_TRY(launch_status());
+  if (M == 0) {
+    // nothing to convert: max |X| over no elements is 0
+    return x_amax_out ? launch_max_small(nullptr, 0, x_amax_out, nullptr, 0.0f, nullptr, st) : FP8MLP_OK;
   }
-  if (M == 0) return FP8MLP_OK;
   uint8_t* Xq = (uint8_t*)workspace;
-  {
-    const int64_t n16 = M * K / 16;   // K % 128 == 0
-    int64_t blocks = cdiv(n16, 256 * 4);
-    if (blocks > 4096) blocks = 4096;
-    TraceScope trace("quantize_e4m3", st);
-    hipLaunchKernelGGL(k_quantize, dim3((unsigned)blocks), dim3(256), 0, st, X, n16, x_scale, Xq, x_amax_out);
-    FP8MLP_TRY(launch_status());
-  }
+  uint32_t* xpart = (uint32_t*)((uint8_t*)workspace + align_up((size_t)(M * K), 256));
+  int64_t nx = 0;
+  FP8MLP_TRY(launch_quantize(X, M * K, x_scale, Xq, x_amax_out ? xpart : nullptr, &nx, st));
   GemmArgs a{Xq, K, Wt_q, N, M, N, K, (int)cdiv(M, CfgLin::BM), (int)cdiv(N, CfgLin::BN), 1, K, 0};
+  if (x_amax_out) {
+    // block 0 of the GEMM finishes max |X| from the conversion's partial maxima
+    a.red_in = xpart;
+    a.red_n = nx;
+    a.red_out = x_amax_out;
+  }
   EpiBf16Out epi{Y, N, 2, nullptr, 0.0f, x_scale, w_inv_scale};
   return launch_gemm<CfgLin, KID_LINEAR>(a, epi, st);
 }

@@ -10,6 +10,9 @@ namespace fp8mlp {
 using CfgUp = GemmCfg<2, 256, 256, 128, 2, 1, KC, KC, 0, 8>;
 // post_q [M,h] . W2t_q [h,d] : e4m3, the cache is read with transposing LDS loads.
 using CfgDown8 = GemmCfg<1, 192, 128, 128, 2, 2, KC, MNC>;
+// Xq [M,d] . W1t_q [d,h] : the up-projection in e4m3 (the W1 cache is read
+// with transposing LDS loads), 256 x 256 tiles, two groups of four waves.
+using CfgUp8 = GemmCfg<1, 256, 256, 128, 2, 1, KC, MNC, 0, 8>;
 // post [M,h] . W2[d,h]^T : bf16 eval path.
 using CfgDownBf16 = GemmCfg<2, 192, 128, 64, 2, 2, KC, KC, true>;
 
@@ -18,6 +21,7 @@ struct FwdPlan {
   size_t partial_bytes;
 };
 static FwdPlan fwd_plan(int64_t M, int64_t h) {
+  static_assert(CfgUp::BM == CfgUp8::BM && CfgUp::BN == CfgUp8::BN, "one partial-amax layout");
   FwdPlan p;
   p.tm = cdiv(M, CfgUp::BM);
   p.tn = cdiv(h, CfgUp::BN);
@@ -100,6 +104,71 @@ int mlp_relu2_fwd(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t
     FP8MLP_TRY(launch_gemm<CfgDownBf16, KID_DOWN_BF16>(a, epi, st));
   }
   return FP8MLP_OK;
+}
+
+size_t mlp_relu2_fwd_fp8up_workspace(int64_t M, int64_t d, int64_t h) {
+  if (M < 0 || d <= 0 || h <= 0) return 0;
+  if (M == 0) return 0;
+  return fwd_plan(M, h).partial_bytes + quantize_partial_bytes() + align_up((size_t)(M * d), 256);
+}
+
+int mlp_relu2_fwd_fp8up(const uint16_t* X, const float* x_scale, const uint8_t* W1t_q, const float* w1_inv_scale,
+                        const uint8_t* W2t_q, const float* w2_inv_scale, const float* amax_prev, float margin,
+                        uint16_t* post, uint8_t* post_q, float* amax_out, float* scale_out, uint16_t* Y,
+                        float* x_amax_out, int64_t M, int64_t d, int64_t h, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  FP8MLP_REQUIRE(M >= 0 && d > 0 && h > 0 && d % 128 == 0 && h % 128 == 0, FP8MLP_E_SHAPE);
+  FP8MLP_REQUIRE(x_scale && W1t_q && w1_inv_scale && W2t_q && w2_inv_scale && amax_prev && amax_out, FP8MLP_E_NULL);
+  if (M > 0) FP8MLP_REQUIRE(X && post && post_q && Y, FP8MLP_E_NULL);
+  FP8MLP_REQUIRE(margin > 0.0f && margin <= 3.4e38f, FP8MLP_E_ARG);
+  for (const void* p : {(const void*)X, (const void*)W1t_q, (const void*)W2t_q, (const void*)post,
+                        (const void*)post_q, (const void*)Y})
+    FP8MLP_REQUIRE(p == nullptr || aligned16(p), FP8MLP_E_ALIGN);
+  for (const void* p : {(const void*)x_scale, (const void*)w1_inv_scale, (const void*)w2_inv_scale,
+                        (const void*)amax_prev, (const void*)amax_out, (const void*)scale_out,
+                        (const void*)x_amax_out})
+    FP8MLP_REQUIRE(((uintptr_t)p & 3) == 0, FP8MLP_E_ALIGN);
+  const FwdPlan plan = fwd_plan(M, h);
+  const size_t need = mlp_relu2_fwd_fp8up_workspace(M, d, h);
+  FP8MLP_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), FP8MLP_E_WORKSPACE);
+  FP8MLP_REQUIRE(need == 0 || aligned16(workspace), FP8MLP_E_ALIGN);
+  FP8MLP_TRY(check_device());
+
+  hipStream_t st = (hipStream_t)stream;
+  if (M == 0) {
+    // no tokens: both maxima are 0 (and the scale that would have been used)
+    if (x_amax_out) FP8MLP_TRY(launch_max_small(nullptr, 0, x_amax_out, nullptr, 0.0f, nullptr, st));
+    return launch_max_small(nullptr, 0, amax_out, amax_prev, margin, scale_out, st);
+  }
+  float* partial = (float*)workspace;
+  uint32_t* xpart = (uint32_t*)((uint8_t*)workspace + plan.partial_bytes);
+  uint8_t* Xq = (uint8_t*)workspace + plan.partial_bytes + quantize_partial_bytes();
+
+  // 1. Xq = e4m3(fp32(X * x_scale)), with per-block maxima of |X| if asked
+  int64_t nx = 0;
+  FP8MLP_TRY(launch_quantize(X, M * d, x_scale, Xq, x_amax_out ? xpart : nullptr, &nx, st));
+  // 2. e4m3 up-projection with the dequantising ReLU^2 / quantise / partial-amax
+  //    epilogue; its block 0 also finishes max |X|
+  {
+    GemmArgs a{Xq, d, W1t_q, h, M, h, d, (int)plan.tm, (int)plan.tn, 1, d};
+    if (x_amax_out) {
+      a.red_in = xpart;
+      a.red_n = nx;
+      a.red_out = x_amax_out;
+    }
+    EpiRelu2QuantT<true> epi{post, post_q, partial, amax_prev, margin, h, (int)plan.tn, x_scale, w1_inv_scale};
+    FP8MLP_TRY(launch_gemm<CfgUp8, KID_UP8>(a, epi, st));
+  }
+  // 3. e4m3 down-projection; its block 0 also finishes the partial amax
+  GemmArgs a{post_q, h, W2t_q, d, M, d, h, (int)cdiv(M, CfgDown8::BM), (int)cdiv(d, CfgDown8::BN), 1, h};
+  a.red_in = (const uint32_t*)partial;
+  a.red_n = plan.tm * plan.tn;
+  a.red_out = amax_out;
+  a.red_amax_prev = amax_prev;
+  a.red_margin = margin;
+  a.red_scale_out = scale_out;
+  EpiBf16Out epi{Y, d, 1, amax_prev, margin, nullptr, w2_inv_scale};
+  return launch_gemm<CfgDown8, KID_DOWN8>(a, epi, st);
 }
 
 }  // extern "C"

@@ -184,12 +184,43 @@ int fp8_scale_from_amax(const float* amax, float margin, float* scale_out, float
  * x_scale, w_inv_scale: device fp32.  x_amax_out: device fp32 or NULL; if
  * given it receives max |X| (for the next step's delayed scale).
  * K: a positive multiple of 128, N: a positive multiple of 64; M >= 0.
- * workspace: fp8_linear_workspace(M, K) bytes (the e4m3 copy of X).
+ * workspace: fp8_linear_workspace(M, K) bytes (the e4m3 copy of X and the
+ * conversion's per-block maxima of |X|).
  * ---------------------------------------------------------------------- */
 size_t fp8_linear_workspace(int64_t M, int64_t K);
 int fp8_linear(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, const float* w_inv_scale,
                uint16_t* Y, float* x_amax_out, int64_t M, int64_t K, int64_t N, void* workspace,
                size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * mlp_relu2_fwd_fp8up -- the TRAIN forward of mlp_relu2_fwd with the
+ * up-projection in e4m3 as well ("NanoGPT Speedrun (Track 1)", "From
+ * Unoptimized", "Approach" item 5: both MLP GEMMs in e4m3 on the training
+ * forward; bf16 backward, bf16 at eval):
+ *   Xq     = e4m3(fp32(X * *x_scale))          (RNE, saturating; in the workspace)
+ *   pre    = fp32(fp32(acc * fp32(1 / *x_scale)) * *w1_inv_scale),
+ *            acc = Xq . W1t_q in fp32           (never stored)
+ *   post, post_q, partial amax, amax_out, scale_out and Y exactly as in
+ *   mlp_relu2_fwd TRAIN (the delayed scale of post from amax_prev, margin).
+ * The pages do not say how X is scaled; x_scale is a per-tensor multiplier the
+ * caller supplies on the device (e.g. fp8_scale_from_amax of the previous
+ * step's x_amax_out with a margin, as for post).
+ * Arguments: X [M, d] bf16; W1t_q [d, h] e4m3, the transposed W1 cache
+ * (fp8_cast_transpose of W1 [h, d]) with its dequantisation multiplier
+ * w1_inv_scale; W2t_q / w2_inv_scale as in mlp_relu2_fwd.  x_amax_out:
+ * device fp32 or NULL; if given it receives max |X|.  d and h: multiples of
+ * 128; M >= 0.  workspace: mlp_relu2_fwd_fp8up_workspace(M, d, h) bytes
+ * (the partial amax tensor, per-block maxima of |X| and the e4m3 copy of X;
+ * 0 for M = 0).  The backward is
+ * mlp_relu2_bwd with the bf16 W1 / W2 and the post written here.
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_ARCH, E_ARG, E_HIP.
+ * ---------------------------------------------------------------------- */
+size_t mlp_relu2_fwd_fp8up_workspace(int64_t M, int64_t d, int64_t h);
+int mlp_relu2_fwd_fp8up(const uint16_t* X, const float* x_scale, const uint8_t* W1t_q, const float* w1_inv_scale,
+                        const uint8_t* W2t_q, const float* w2_inv_scale, const float* amax_prev, float margin,
+                        uint16_t* post, uint8_t* post_q, float* amax_out, float* scale_out, uint16_t* Y,
+                        float* x_amax_out, int64_t M, int64_t d, int64_t h, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* ------------------------------------------------------------------------
  * Layer-stack helpers.  The speedrun pages train the MLP block inside a

@@ -154,3 +154,39 @@ def test_bwd_ragged_mid_size(fm):
         assert rel_fro(dx[i], bs["dX_rows"][i]) < 1e-2, rows[i]
     assert rel_fro(dW1.cpu().numpy()[[0, 2000]].astype(np.float64), bs["dW1_rows"]) < 4e-3
     assert rel_fro(dW2.cpu().numpy()[:, [5, h - 1]].astype(np.float64), bs["dW2_cols"]) < 1e-4
+
+
+def test_fp8up_full_size_sampled(fm):
+    """The e4m3 up-projection forward at the timed workload's size
+    (M=49152, d=768, h=3072) through Relu2MLP(fp8_up=True): amaxes
+    bit-exact over whole tensors, both weight caches bit-exact, sampled rows
+    of post within the per-element bound, their codes bit-exact, Y close to
+    the oracle's FP8 GEMM of the GPU's codes."""
+    from .test_gpu_fp8up import post_bound
+    M, d, h = synth.WORKLOADS["fwdbwd"][:3]
+    seed = synth.WORKLOADS["fwdbwd"][3]
+    ins = synth.mlp_inputs(M, d, h, seed)
+    case(f"full-size fp8-up forward M={M} d={d} h={h}")
+    blk = fm.Relu2MLP(bf16_dev(ins["W1"]), bf16_dev(ins["W2"]), margin=2.0, amax_init=1.0, fp8_up=True)
+    X = bf16_dev(ins["X"])
+    blk.forward(X)                                   # bootstrap both amaxes
+    xa, a = float(blk.x_amax_prev.item()), float(blk.amax_prev.item())
+    Y, post, post_q = blk.forward(X)
+    torch.cuda.synchronize()
+    Xf_max = max(float(np.abs(F.bf16_to_f64(ins["X"][r0:r0 + 8192])).max()) for r0 in range(0, M, 8192))
+    assert f32_bits(xa) == f32_bits(Xf_max) and f32_bits(blk.x_amax_prev.item()) == f32_bits(Xf_max)
+    post_b = bits(post)
+    assert f32_bits(blk.amax_last.item()) == f32_bits(_max_bf16_nonneg(post_b))
+    sx, s = O.delayed_scale(xa, 2.0), O.delayed_scale(a, 2.0)
+    assert f32_bits(blk.x_scale.item()) == f32_bits(sx) and f32_bits(blk.scale_used.item()) == f32_bits(s)
+    W1t, _, inv1, _ = O.cast_transpose(ins["W1"])
+    W2t, _, inv2, _ = O.cast_transpose(ins["W2"])
+    assert (W1t == blk.W1t_q.cpu().numpy()).all() and (W2t == blk.W2t_q.cpu().numpy()).all()
+    rows = np.concatenate([np.arange(0, M, 1009), [255, 256, M - 1]])
+    pb = F.bf16_to_f64(post_b[rows])
+    ref_post, _, _ = O.up_relu2_fp8(ins["X"][rows], sx, W1t, inv1)
+    assert (np.abs(pb - ref_post) <= post_bound(ins["X"][rows], sx, W1t, inv1)).all()
+    pq = post_q.cpu().numpy()[rows]
+    assert (O.quantize(pb, s) == pq).all()
+    y = F.bf16_to_f64(bits(Y)[rows])
+    assert rel_fro(y, O.down_fp8(pq, W2t, O.inv_scale(s), inv2)) < 4e-3
