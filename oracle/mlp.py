@@ -85,6 +85,21 @@ def inv_scale(scale):
     return float(fl32(1.0 / np.float64(np.float32(scale))))
 
 
+def window_scale(amax_history, margin):
+    """Rolling-window variant of the delayed scale: the scale of the largest
+    amax among the last L steps ([R] delayed-scaling paragraph names the
+    rolling window as the alternative to amax(t-1); L = 1 is amax(t-1)).
+    NaN anywhere in the window propagates, as in ``amax``."""
+    return delayed_scale(amax(np.asarray(amax_history, dtype=np.float64)), margin)
+
+
+def saturation_count(codes):
+    """Number of e4m3 codes whose value has magnitude 448 (the top code):
+    the clip-rate telemetry of a delayed scale."""
+    v = e4m3_decode(np.asarray(codes, dtype=np.uint8))
+    return int(np.count_nonzero(np.abs(v) == E4M3_MAX))
+
+
 # --------------------------------------------------------------------------
 # weight cache: cast + transpose
 # --------------------------------------------------------------------------
@@ -101,6 +116,15 @@ def cast_transpose(W_bits, scale_in=None):
     s = exact_scale(a) if scale_in is None else float(np.float32(scale_in))
     codes = e4m3_encode(fl32(W * s))
     return np.ascontiguousarray(codes.T), s, inv_scale(s), a
+
+
+def delayed_cast_transpose(W_bits, amax_w_prev, margin):
+    """Delayed-scale variant of the weight-cache refresh: the scale comes from
+    the previous refresh's max|W| times a margin instead of the exact max|W|
+    of the weights being cast ([R] implementation notes: the exact refresh is
+    the viable choice because W2 is small; this is the alternative).
+    Returns (codes, scale, inv_scale, amax of the new W)."""
+    return cast_transpose(W_bits, scale_in=delayed_scale(amax_w_prev, margin))
 
 
 # --------------------------------------------------------------------------

@@ -370,3 +370,41 @@ def test_fp8_up_forward_composes_like_train_forward():
     for k in ("post_q", "y"):
         assert (out[k] == ref[k]).all()
     assert out["scale"] == ref["scale"] == O.delayed_scale(3.0, 2.0)
+
+
+# ------------------------------------------------------------------ scaling policies
+def test_saturation_count_is_the_top_code_count():
+    codes = np.arange(256, dtype=np.uint8)
+    assert O.saturation_count(codes) == 2                  # 0x7E and 0xFE
+    assert O.saturation_count(np.array([0x7E, 0xFE, 0x7F, 0xFF, 0x7D], dtype=np.uint8)) == 2
+    # through the quantiser: exactly the products >= 432 (the midpoint between
+    # 416 and 448 rounds to the even code 448, and everything above saturates)
+    g = np.random.default_rng(31)
+    post = F.bf16(np.abs(g.standard_normal(200000)) ** 2)
+    s = O.delayed_scale(float(post.max()) / 3, 2.0)
+    q = O.quantize(post, s)
+    v = (post * s).astype(np.float32).astype(np.float64)
+    assert O.saturation_count(q) == int(np.count_nonzero(v >= 432.0)) > 0
+    assert O.saturation_count(O.quantize(np.array([431.9, 432.0, 500.0]), 1.0)) == 2
+
+
+def test_window_scale_special_cases():
+    assert O.window_scale([3.0], 2.0) == O.delayed_scale(3.0, 2.0)
+    assert O.window_scale([1.0, 5.0, 2.0], 2.0) == O.delayed_scale(5.0, 2.0)
+    assert O.window_scale([0.0, 0.0], 2.0) == 1.0                  # guard
+    assert O.window_scale([1.0, float("nan")], 2.0) == 1.0         # NaN propagates to the guard
+    # a window never gives a larger scale than amax(t-1) alone
+    h = [0.5, 4.0, 1.5]
+    assert O.window_scale(h, 2.0) <= O.delayed_scale(h[-1], 2.0)
+
+
+def test_delayed_cast_with_its_own_amax_is_the_exact_cast():
+    W = synth.mlp_inputs(8, 64, 128, 32)["W2"]
+    a = O.amax(F.bf16_to_f64(W))
+    c1 = O.cast_transpose(W)
+    c2 = O.delayed_cast_transpose(W, a, 1.0)
+    assert (c1[0] == c2[0]).all() and c1[1:] == c2[1:]
+    # a larger previous amax gives a smaller scale and codes that never saturate
+    c3 = O.delayed_cast_transpose(W, 2 * a, 1.5)
+    assert c3[1] == O.delayed_scale(2 * a, 1.5) < c1[1]
+    assert O.saturation_count(c3[0]) == 0
