@@ -44,7 +44,8 @@ OTHER_NAMES = {"k_max_final": "amax_final", "k_amax_partial": "amax_partial", "k
                "k_splitk_reduce": "splitk_reduce", "k_quantize": "quantize_e4m3", "k_fill_zero": "fill_zero",
                "k_zero_scalar": "zero_scalar", "k_scale_from_amax": "scale_from_amax", "k_amax_small": "amax_small",
                "k_transpose_weights": "transpose_weights", "k_rmsnorm_fwd": "rmsnorm_fwd", "k_rmsnorm_bwd": "rmsnorm_bwd",
-               "k_add_bf16": "add_bf16", "k_sgd_bf16": "sgd_update_bf16", "k_mfma_probe": "mfma_probe"}
+               "k_add_bf16": "add_bf16", "k_sgd_bf16": "sgd_update_bf16", "k_mfma_probe": "mfma_probe",
+               "k_count_top": "count_top_codes", "k_sum_counts": "sum_counts"}
 
 
 def log(msg):
@@ -461,8 +462,8 @@ def extra_measurements(fm, torch, dev, X, W1, W2, dY, blk, post, post_q, Y, dX, 
     Xs = [bfd(b["X"]) for b in batches]
     dYs = [bfd(b["dY"]) for b in batches]
 
-    def stack_run(clip=None):
-        stk = Relu2Stack([bfd(w1) for w1, _ in wts], [bfd(w2) for _, w2 in wts], lr=synth.STACK["lr"])
+    def stack_run(clip=None, **opts):
+        stk = Relu2Stack([bfd(w1) for w1, _ in wts], [bfd(w2) for _, w2 in wts], lr=synth.STACK["lr"], **opts)
         stk.step(Xs[0], dYs[0])            # allocation + the bootstrap step, untimed
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -485,6 +486,27 @@ def extra_measurements(fm, torch, dev, X, W1, W2, dY, blk, post, post_q, Y, dX, 
     out["stack_12x8_mixed_floor_ms"] = round(floor_stack, 2)
     out["stack_clip_fraction_max"] = max(max(r) for r in clip)
     out["stack_clip_fraction_nonzero_layer_steps"] = sum(1 for r in clip for v in r if v > 0)
+    t_stack8 = stack_run(fp8_up=True)
+    out["stack_12x8_fp8up_ms"] = round(t_stack8, 2)
+    out["stack_12x8_fp8up_tflops"] = round(fl_stack / (t_stack8 * 1e-3) / 1e12, 1)
+
+    # margin / window sweep with the top-code telemetry (share of e4m3 post
+    # codes at 448 per layer and step, bootstrap step excluded)
+    sweep = []
+    for margin, window in ((1.0, 1), (1.25, 1), (2.0, 1), (4.0, 1), (1.25, 4)):
+        stk = Relu2Stack([bfd(w1) for w1, _ in wts], [bfd(w2) for _, w2 in wts], lr=synth.STACK["lr"],
+                         margin=margin, amax_window=window, telemetry=True)
+        stk.step(Xs[0], dYs[0])
+        rates = []
+        for t in range(steps_s):
+            stk.step(Xs[t], dYs[t])
+            rates.append(stk.saturated.double().cpu().numpy() / (Ms * hs))
+        r = np.stack(rates)
+        sweep.append({"margin": margin, "window": window, "top_code_rate_max": float(r.max()),
+                      "top_code_rate_mean": float(r.mean()),
+                      "layer_steps_with_top_codes": int(np.count_nonzero(r))})
+        del stk
+    out["margin_sweep"] = sweep
     del Xs, dYs
 
     # FP8 attention projections: QKV [49152,768]x[768,2304], O [49152,768]x[768,768]

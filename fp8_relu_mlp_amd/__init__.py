@@ -8,7 +8,8 @@ is not built, the first call raises.
 
 Entry points (same names as the C ABI):
   mlp_relu2_fwd, mlp_relu2_fwd_fp8up, mlp_relu2_bwd, fp8_cast_transpose, fp8_cast_transpose_w2,
-  amax_reduce, fp8_scale_from_amax, fp8_linear, and the layer-stack helpers
+  amax_reduce, fp8_scale_from_amax, fp8_linear, fp8_saturation_count, and the
+  layer-stack helpers
   rmsnorm_fwd, rmsnorm_bwd, add_bf16, sgd_update_bf16
 and ``Relu2MLP``, one MLP block's device state (bf16 weights, the transposed
 fp8 W2 cache with its scales, the delayed-scale amax carried between steps);
@@ -24,7 +25,7 @@ F32 = 0
 BF16 = 1
 
 __all__ = ["mlp_relu2_fwd", "mlp_relu2_fwd_fp8up", "mlp_relu2_bwd", "fp8_cast_transpose", "fp8_cast_transpose_w2", "amax_reduce",
-           "fp8_scale_from_amax", "fp8_linear", "rmsnorm_fwd", "rmsnorm_bwd", "add_bf16", "sgd_update_bf16",
+           "fp8_scale_from_amax", "fp8_linear", "fp8_saturation_count", "rmsnorm_fwd", "rmsnorm_bwd", "add_bf16", "sgd_update_bf16",
            "Relu2MLP", "KernelTimer", "Fp8MlpError", "TRAIN_FP8", "EVAL_BF16"]
 
 
@@ -145,6 +146,16 @@ def fp8_linear(X, x_scale, Wt_q, w_inv_scale, Y, x_amax_out=None, workspace=None
         _stream(stream)))
 
 
+def fp8_saturation_count(q, count_out, workspace=None, stream=None):
+    """count_out (1-element int64 device tensor) = number of e4m3 codes of
+    magnitude 448 in the uint8 tensor q (clip-rate telemetry)."""
+    n = q.numel()
+    L = lib()
+    ws, wsb = _ws(L.fp8_saturation_count_workspace(n), workspace, q.device)
+    check("fp8_saturation_count", L.fp8_saturation_count(_p(q) if n else None, n, _p(count_out), _p(ws), wsb,
+                                                         _stream(stream)))
+
+
 def rmsnorm_fwd(x, xn, inv_rms, eps=1e-6, stream=None):
     """xn = bf16(x * r), r = 1/sqrt(mean(x^2) + eps) per row -> inv_rms [M] fp32."""
     M, d = x.shape
@@ -237,19 +248,40 @@ class Relu2MLP:
     cache W1t_q [d,h] (``refresh_caches`` renews both caches) and the amax of
     its input X from the previous step (``x_amax_prev``), from which each
     forward derives the input's scale with the same margin.
+
+    Scaling policies (the alternatives the delayed-scaling paragraph of "A
+    Retrospective on Our World Records" weighs): ``amax_window`` = L > 1
+    takes the activation scale from the maximum of the last L measured amaxes
+    (a rolling window) instead of amax(t-1) alone; ``w2_scale="delayed"``
+    casts W2 with the scale of the previous refresh's max|W2| times
+    ``w2_margin`` instead of the exact max|W2| of the weights being cast (the
+    first refresh is exact).
     """
 
-    def __init__(self, W1, W2, margin=2.0, amax_init=None, fp8_up=False, x_amax_init=None):
+    def __init__(self, W1, W2, margin=2.0, amax_init=None, fp8_up=False, x_amax_init=None, amax_window=1,
+                 w2_scale="exact", w2_margin=1.0):
         dev = W1.device
         self.W1, self.W2, self.margin = W1, W2, float(margin)
         h, d = W1.shape
         self.d, self.h = d, h
         f = lambda: torch.zeros(1, dtype=torch.float32, device=dev)
+        if int(amax_window) < 1:
+            raise ValueError("amax_window must be >= 1")
+        if w2_scale not in ("exact", "delayed"):
+            raise ValueError("w2_scale is 'exact' or 'delayed'")
+        self.amax_window, self.w2_policy, self.w2_margin = int(amax_window), w2_scale, float(w2_margin)
+        # rolling window: the last L measured amaxes, written in turn
+        self.amax_hist = torch.zeros(self.amax_window, dtype=torch.float32, device=dev)
+        self._hist_pos = 0
+        self.amax_last_measured = None
         self.w2_scale, self.w2_inv_scale, self.w2_amax = f(), f(), f()
+        self._w2_amax_next, self._w2_scale_in = f(), f()
+        self._w2_refreshed = False
         self.W2t_q = torch.empty((h, d), dtype=torch.uint8, device=dev)
         self.amax_prev, self._amax_next, self.scale_used = f(), f(), f()
         if amax_init is not None:
             self.amax_prev.fill_(float(amax_init))
+        self.amax_last_measured = self.amax_prev
         self.fp8_up = bool(fp8_up)
         if self.fp8_up:
             self.w1_scale, self.w1_inv_scale, self.w1_amax = f(), f(), f()
@@ -260,8 +292,16 @@ class Relu2MLP:
         self.refresh_caches()
 
     def refresh_w2_cache(self, workspace=None, stream=None):
-        fp8_cast_transpose_w2(self.W2, self.W2t_q, self.w2_scale, self.w2_inv_scale, self.w2_amax,
-                              workspace=workspace, stream=stream)
+        if self.w2_policy == "exact" or not self._w2_refreshed:
+            fp8_cast_transpose_w2(self.W2, self.W2t_q, self.w2_scale, self.w2_inv_scale, self.w2_amax,
+                                  workspace=workspace, stream=stream)
+        else:
+            # delayed: the scale comes from the previous refresh's max|W2|
+            fp8_scale_from_amax(self.w2_amax, self.w2_margin, self._w2_scale_in, stream=stream)
+            fp8_cast_transpose(self.W2, self.W2t_q, self._w2_scale_in, self.w2_scale, self.w2_inv_scale,
+                               self._w2_amax_next, workspace=workspace, stream=stream)
+            self.w2_amax, self._w2_amax_next = self._w2_amax_next, self.w2_amax
+        self._w2_refreshed = True
 
     def refresh_caches(self, workspace=None, stream=None):
         """Renew the e4m3 weight caches after an update of W2 (and of W1 with fp8_up)."""
@@ -280,25 +320,32 @@ class Relu2MLP:
         if mode == TRAIN_FP8 and post_q is None:
             post_q = torch.empty((M, self.h), dtype=torch.uint8, device=dev)
         Y = torch.empty((M, self.d), dtype=torch.bfloat16, device=dev) if Y is None else Y
+        # with a window the measured amax lands in the next slot of the history
+        windowed = carry and self.amax_window > 1
+        amax_out = self.amax_hist[self._hist_pos:self._hist_pos + 1] if windowed else self._amax_next
         if mode == TRAIN_FP8 and self.fp8_up:
             fp8_scale_from_amax(self.x_amax_prev, self.margin, self.x_scale, stream=stream)
             mlp_relu2_fwd_fp8up(X, self.x_scale, self.W1t_q, self.w1_inv_scale, self.W2t_q, self.w2_inv_scale,
-                                self.amax_prev, self.margin, post, post_q, self._amax_next, self.scale_used, Y,
+                                self.amax_prev, self.margin, post, post_q, amax_out, self.scale_used, Y,
                                 x_amax_out=self._x_amax_next, workspace=workspace, stream=stream)
             if carry:
                 self.x_amax_prev, self._x_amax_next = self._x_amax_next, self.x_amax_prev
         else:
             mlp_relu2_fwd(mode, X, self.W1, self.W2t_q, self.w2_inv_scale, self.W2, self.amax_prev, self.margin,
-                          post, post_q if mode == TRAIN_FP8 else None, self._amax_next,
+                          post, post_q if mode == TRAIN_FP8 else None, amax_out,
                           self.scale_used if mode == TRAIN_FP8 else None, Y, workspace=workspace, stream=stream)
-        if carry:
+        if windowed:
+            self.amax_last_measured = amax_out
+            self._hist_pos = (self._hist_pos + 1) % self.amax_window
+            amax_reduce(self.amax_hist, self.amax_prev, stream=stream)
+        elif carry:
             self.amax_prev, self._amax_next = self._amax_next, self.amax_prev
         return Y, post, post_q
 
     @property
     def amax_last(self):
         """The amax measured by the most recent carried forward."""
-        return self.amax_prev
+        return self.amax_last_measured if self.amax_window > 1 else self.amax_prev
 
     def backward(self, dY, X, post, dX=None, dW1=None, dW2=None, accumulate=False, workspace=None, stream=None):
         dev = X.device

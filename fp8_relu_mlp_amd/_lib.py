@@ -37,6 +37,8 @@ SIGNATURES = {
     "amax_reduce_workspace": (c_size, [c_i64]),
     "amax_reduce": (c_int, [c_int, vp, c_i64, vp, vp, c_size, vp]),
     "fp8_scale_from_amax": (c_int, [vp, c_float, vp, vp, vp]),
+    "fp8_saturation_count_workspace": (c_size, [c_i64]),
+    "fp8_saturation_count": (c_int, [vp, c_i64, vp, vp, c_size, vp]),
     "fp8_linear_workspace": (c_size, [c_i64, c_i64]),
     "fp8_linear": (c_int, [vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, vp, c_size, vp]),
     "rmsnorm_fwd": (c_int, [vp, vp, vp, c_i64, c_i64, c_float, vp]),

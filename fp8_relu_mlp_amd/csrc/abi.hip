@@ -236,6 +236,46 @@ __global__ void __launch_bounds__(256) k_cast_transpose(const uint16_t* __restri
   }
 }
 
+// ------------------------------------------------------------------ saturation count
+// Number of e4m3 codes of magnitude 448 (0x7E, 0xFE): the top code, which every
+// value from 432 up (after scaling) receives, clipped or not.  Per-block
+// counts go to partial[], a one-block pass adds them up.
+__device__ __forceinline__ uint32_t top_codes_in_word(uint32_t w) {
+  const uint32_t y = (w & 0x7f7f7f7fu) ^ 0x7e7e7e7eu;          // byte 0 <=> top code
+  const uint32_t nz = ((y & 0x7f7f7f7fu) + 0x7f7f7f7fu) | y;    // bit 7 of a byte: byte != 0
+  return (uint32_t)__builtin_popcount(~nz & 0x80808080u);
+}
+
+__global__ void __launch_bounds__(256) k_count_top(const i32x4* __restrict__ q, int64_t n16,
+                                                   uint32_t* __restrict__ partial) {
+  __shared__ uint32_t red[4];
+  uint32_t c = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) {
+    const i32x4 v = __builtin_nontemporal_load(q + i);
+    c += top_codes_in_word((uint32_t)v[0]) + top_codes_in_word((uint32_t)v[1]) + top_codes_in_word((uint32_t)v[2]) +
+         top_codes_in_word((uint32_t)v[3]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ void __launch_bounds__(256) k_sum_counts(const uint32_t* __restrict__ partial, int n,
+                                                    unsigned long long* out) {
+  __shared__ unsigned long long red[4];
+  unsigned long long c = 0;
+  for (int i = threadIdx.x; i < n; i += 256) c += partial[i];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) *out = red[0] + red[1] + red[2] + red[3];
+}
+
+constexpr int kCountBlocks = 2048;
+
 }  // namespace fp8mlp
 
 using namespace fp8mlp;
@@ -320,6 +360,33 @@ int fp8_cast_transpose_w2(const uint16_t* W2, int64_t d, int64_t h, uint8_t* W2t
                           void* stream) {
   return fp8_cast_transpose(W2, d, h, W2t_q, nullptr, scale_out, inv_scale_out, amax_out, workspace,
                             workspace_bytes, stream);
+}
+
+size_t fp8_saturation_count_workspace(int64_t n) { return n <= 0 ? 0 : (size_t)kCountBlocks * 4; }
+
+int fp8_saturation_count(const uint8_t* q, int64_t n, uint64_t* count_out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  FP8MLP_REQUIRE(n >= 0 && n % 16 == 0, FP8MLP_E_SHAPE);
+  FP8MLP_REQUIRE(count_out && (q || n == 0), FP8MLP_E_NULL);
+  FP8MLP_REQUIRE((q == nullptr || aligned16(q)) && ((uintptr_t)count_out & 7) == 0, FP8MLP_E_ALIGN);
+  const size_t need = fp8_saturation_count_workspace(n);
+  FP8MLP_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), FP8MLP_E_WORKSPACE);
+  FP8MLP_REQUIRE(need == 0 || aligned16(workspace), FP8MLP_E_ALIGN);
+  FP8MLP_TRY(check_device());
+  const hipStream_t st = (hipStream_t)stream;
+  int64_t blocks = 0;
+  if (n > 0) {
+    blocks = cdiv(n / 16, 256 * 4);
+    if (blocks > kCountBlocks) blocks = kCountBlocks;
+    TraceScope trace("count_top_codes", st);
+    hipLaunchKernelGGL(k_count_top, dim3((unsigned)blocks), dim3(256), 0, st, (const i32x4*)q, n / 16,
+                       (uint32_t*)workspace);
+    FP8MLP_TRY(launch_status());
+  }
+  TraceScope trace("sum_counts", st);
+  hipLaunchKernelGGL(k_sum_counts, dim3(1), dim3(256), 0, st, (const uint32_t*)workspace, (int)blocks,
+                     (unsigned long long*)count_out);
+  return launch_status();
 }
 
 }  // extern "C"

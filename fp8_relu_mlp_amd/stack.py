@@ -28,19 +28,29 @@ scale and writes the amax it measures, which becomes ``amax_prev`` for the
 next step (a buffer swap inside ``Relu2MLP``).  The very first step has no
 previous amax: each layer first runs one forward to measure the exact amax of
 that step and then runs again with it.
+
+Options passed to every block: ``fp8_up`` (both forward GEMMs in e4m3; the
+W1 cache is refreshed after each update as well), ``amax_window`` and
+``w2_scale`` / ``w2_margin`` (the scaling policies of ``Relu2MLP``).  With
+``telemetry`` each layer's forward is followed by fp8_saturation_count on its
+e4m3 post copy; ``saturated`` [L] (int64, device) holds the counts of the
+last step and ``saturation_rate(l)`` their share of the M*h codes.
 """
 import numpy as np
 import torch
 
-from . import (TRAIN_FP8, Relu2MLP, add_bf16, lib, rmsnorm_bwd, rmsnorm_fwd,
-               sgd_update_bf16)
+from . import (TRAIN_FP8, Relu2MLP, add_bf16, fp8_saturation_count, lib,
+               rmsnorm_bwd, rmsnorm_fwd, sgd_update_bf16)
 
 
 class Relu2Stack:
-    def __init__(self, W1s, W2s, margin=2.0, lr=1e-3, eps=1e-6, loss="mean"):
+    def __init__(self, W1s, W2s, margin=2.0, lr=1e-3, eps=1e-6, loss="mean", fp8_up=False, amax_window=1,
+                 w2_scale="exact", w2_margin=1.0, telemetry=False):
         if len(W1s) != len(W2s) or not W1s:
             raise ValueError("need the same positive number of W1 and W2 tensors")
-        self.layers = [Relu2MLP(w1, w2, margin=margin, amax_init=1.0) for w1, w2 in zip(W1s, W2s)]
+        self.layers = [Relu2MLP(w1, w2, margin=margin, amax_init=1.0, fp8_up=fp8_up, amax_window=amax_window,
+                                w2_scale=w2_scale, w2_margin=w2_margin) for w1, w2 in zip(W1s, W2s)]
+        self.fp8_up, self.telemetry = bool(fp8_up), bool(telemetry)
         self.L = len(self.layers)
         self.d, self.h = self.layers[0].d, self.layers[0].h
         if loss not in ("mean", "sum"):
@@ -67,9 +77,14 @@ class Relu2Stack:
         self.dW2 = torch.empty((d, h), dtype=f32, device=dev)
         Lb = lib()
         u8 = torch.uint8
-        self.ws_f = torch.empty(max(1, Lb.mlp_relu2_fwd_workspace(M, d, h)), dtype=u8, device=dev)
+        ws_fwd = Lb.mlp_relu2_fwd_workspace(M, d, h)
+        if self.fp8_up:
+            ws_fwd = max(ws_fwd, Lb.mlp_relu2_fwd_fp8up_workspace(M, d, h))
+        self.ws_f = torch.empty(max(1, ws_fwd), dtype=u8, device=dev)
         self.ws_b = torch.empty(max(1, Lb.mlp_relu2_bwd_workspace(M, d, h)), dtype=u8, device=dev)
         self.ws_c = torch.empty(max(1, Lb.fp8_cast_transpose_workspace(d, h)), dtype=u8, device=dev)
+        self.ws_t = torch.empty(max(1, Lb.fp8_saturation_count_workspace(M * h)), dtype=u8, device=dev)
+        self.saturated = torch.zeros((self.L,), dtype=torch.int64, device=dev)
         # per step and layer: amax_prev used, scale used, amax measured
         self.state = torch.zeros((self.L, 3), dtype=f32, device=dev)
         self.lr_step = float(np.float32(self.lr / M if self.loss == "mean" else self.lr))
@@ -96,6 +111,8 @@ class Relu2Stack:
                         workspace=self.ws_f)
             self.state[l, 1].copy_(blk.scale_used[0])
             self.state[l, 2].copy_(blk.amax_last[0])
+            if self.telemetry:
+                fp8_saturation_count(self.post_q, self.saturated[l:l + 1], workspace=self.ws_t)
             add_bf16(self.x[l], self.Y, self.x[l + 1])
             if observe:
                 observe(l, "fwd", self)
@@ -110,11 +127,16 @@ class Relu2Stack:
                 observe(l, "bwd", self)
             sgd_update_bf16(blk.W1, self.dW1, self.lr_step)
             sgd_update_bf16(blk.W2, self.dW2, self.lr_step)
-            blk.refresh_w2_cache(workspace=self.ws_c)
+            blk.refresh_caches(workspace=self.ws_c)
             if observe:
                 observe(l, "upd", self)
         self.steps_done += 1
         return self.state
+
+    def saturation_rate(self, l):
+        """Share of layer l's e4m3 post codes at the top code (448) in the
+        last step (needs telemetry=True)."""
+        return float(self.saturated[l].item()) / float(self._M * self.h)
 
     def clip_fraction(self, l):
         """Share of layer l's last post values that the e4m3 copy saturated

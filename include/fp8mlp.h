@@ -175,6 +175,23 @@ int amax_reduce(int dtype, const void* x, int64_t n, float* amax_out, void* work
 int fp8_scale_from_amax(const float* amax, float margin, float* scale_out, float* inv_scale_out, void* stream);
 
 /* ------------------------------------------------------------------------
+ * fp8_saturation_count -- clip-rate telemetry for a delayed scale ("A
+ * Retrospective on Our World Records", Main Track: the scale from amax(t-1)
+ * times a safety margin; the margin bounds how far the activation may grow
+ * in one step before the e4m3 copy clips):
+ *   count_out = number of codes among q[0 .. n) of magnitude 448 (0x7E, 0xFE)
+ * 448 is the top e4m3 code: every scaled value from 432 up receives it, and
+ * values above 464 would not fit at all (saturated), so the count bounds the
+ * clipped share from above and is 0 whenever nothing came near the limit.
+ * q: device e4m3 codes, n a multiple of 16 (0 gives 0).  count_out: device
+ * uint64, 8-byte aligned.  workspace: fp8_saturation_count_workspace(n) bytes.
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_ARCH, E_HIP.
+ * ---------------------------------------------------------------------- */
+size_t fp8_saturation_count_workspace(int64_t n);
+int fp8_saturation_count(const uint8_t* q, int64_t n, uint64_t* count_out, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* ------------------------------------------------------------------------
  * fp8_linear -- forward of an FP8 projection ("NanoGPT Speedrun (Track 1)",
  * "Changes vs Record #83" item 1: QKV and output projections in e4m3 on the
  * forward pass, weights stored transposed):
