@@ -268,6 +268,19 @@ def mlp_bwd(dY_bits, X_bits, W1_bits, W2_bits, post, rnd=bf16):
     return {"dX": dX, "dW1": dW1, "dW2": dW2, "dpre": dpre}
 
 
+def post_from_q(q_codes, scale):
+    """The backward's stand-in for post when only its e4m3 copy was kept:
+    post_hat = fl32(dec(q) * fl32(1/scale)).
+
+    [R] implementation notes: the BF16 post stays materialised by choice;
+    rebuilding what the backward needs from the FP8 copy is the orthogonal
+    variant.  Reading: post_hat replaces post everywhere in ``mlp_bwd``
+    (sqrt(post_hat) in dpre, post_hat in dW2).  dec(q) (<= 4 significant
+    bits) times an fp32 value is exact in float64, so ``fl32`` rounds once.
+    """
+    return fl32(e4m3_decode(np.asarray(q_codes, dtype=np.uint8)) * inv_scale(scale))
+
+
 def mlp_bwd_sampled(dY_bits, X_bits, W1_bits, W2_bits, post, rows, dw1_rows,
                     dw2_cols, rnd=bf16):
     """The same formulas as ``mlp_bwd`` evaluated only on sampled outputs.

@@ -408,3 +408,34 @@ def test_delayed_cast_with_its_own_amax_is_the_exact_cast():
     c3 = O.delayed_cast_transpose(W, 2 * a, 1.5)
     assert c3[1] == O.delayed_scale(2 * a, 1.5) < c1[1]
     assert O.saturation_count(c3[0]) == 0
+
+
+# ------------------------------------------------------------------ backward from the e4m3 copy
+def test_post_from_q_inverts_the_lossless_quantisation():
+    X, W1, _ = _lossless_case()
+    post = O.up_relu2(X, W1)
+    assert post.max() == 9.0
+    q = O.quantize(post, 32.0)
+    assert (O.post_from_q(q, 32.0) == post).all()
+
+
+def test_post_from_q_within_the_e4m3_step():
+    """e4m3 keeps 4 significant bits: for scaled values in the normal range
+    the decoded copy is within 2^-4 relative of post (half a step), below it
+    within half the subnormal step 2^-10 / scale; plus one fp32 rounding."""
+    g = np.random.default_rng(41)
+    post = F.bf16(np.abs(g.standard_normal(100000)) ** 2)
+    s = O.delayed_scale(float(post.max()), 2.0)
+    ph = O.post_from_q(O.quantize(post, s), s)
+    bound = np.maximum(2.0 ** -4 * post, 2.0 ** -10 / s) * (1 + 2.0 ** -20)
+    assert (np.abs(ph - post) <= bound).all()
+    assert np.abs(ph - post).max() > 0
+    # the bf16-path backward on post_hat equals the calculus one on post_hat
+    ins = synth.mlp_inputs(6, 32, 64, 42, with_dy=True)
+    post = O.up_relu2(ins["X"], ins["W1"])
+    s = O.delayed_scale(float(post.max()), 2.0)
+    ph = O.post_from_q(O.quantize(post, s), s)
+    a = O.mlp_bwd(ins["dY"], ins["X"], ins["W1"], ins["W2"], ph, rnd=O.exact)
+    dY, W2 = F.bf16_to_f64(ins["dY"]), F.bf16_to_f64(ins["W2"])
+    assert np.allclose(a["dW2"], dY.T @ ph, rtol=0, atol=1e-12)
+    assert np.allclose(a["dpre"], 2 * np.sqrt(ph) * (dY @ W2), rtol=0, atol=1e-12)
