@@ -385,7 +385,8 @@ def extra_measurements(fm, torch, dev, X, W1, W2, dY, blk, post, post_q, Y, dX, 
     """Side measurements (not part of `value`): forward-only TRAIN vs EVAL
     (bf16 down-projection ablation), the W2 cache refresh, the step with the
     up-projection in e4m3 as well (mlp_relu2_fwd_fp8up, both weight caches
-    refreshed after the update), the layer-stack
+    refreshed after the update), the step that keeps only the e4m3 copy of
+    post (mlp_relu2_bwd_fp8post), the layer-stack
     workload (12 layers x 8 SGD steps at M=65536, with the share of post
     values the e4m3 copy clipped per layer and step) and the FP8 attention
     projections."""
@@ -448,6 +449,48 @@ def extra_measurements(fm, torch, dev, X, W1, W2, dY, blk, post, post_q, Y, dX, 
     if xq:
         out["fp8up_quantize_x_us"] = round(1e3 * sum(xq) / len(xq), 2)
     del blk8, ws_8
+
+    # the step without the bf16 post: the backward runs on the e4m3 copy
+    blkq = fm.Relu2MLP(W1, W2, margin=MARGIN, amax_init=1.0, keep_post=False)
+    blkq.forward(X, post_q=post_q, Y=Y, workspace=ws_f)
+
+    def stepq():
+        blkq.forward(X, post_q=post_q, Y=Y, workspace=ws_f)
+        blkq.backward(dY, X, None, dX, dW1, dW2, workspace=ws_b, post_q=post_q)
+        blkq.refresh_w2_cache(workspace=ws_c)
+
+    t_fq = timed(lambda: blkq.forward(X, post_q=post_q, Y=Y, carry=False, workspace=ws_f))
+    t_sq = timed(stepq)
+    out["fp8post_fwd_ms"] = round(t_fq, 4)
+    out["fp8post_step_ms"] = round(t_sq, 4)
+    out["fp8post_step_tflops"] = round(6 * mdh2 / (t_sq * 1e-3) / 1e12, 1)
+    out["fp8post_step_pct_mixed_mfma_peak"] = round(100.0 * mixed_floor_us(M, D, H) / (t_sq * 1e3), 2)
+    with fm.KernelTimer(64 * reps) as kt:
+        for _ in range(reps):
+            stepq()
+    torch.cuda.synchronize()
+    perq = {}
+    for name, t in kt.records():
+        perq.setdefault(name, []).append(t)
+    out["fp8post_kernels_us"] = {k: round(1e3 * sum(v) / len(v), 2) for k, v in perq.items()
+                                 if k in ("up_gemm_relu2_quant", "dpost_gemm_dpre", "dw2_gemm")}
+    del blkq
+
+    # both variants together: e4m3 up-projection, no bf16 post
+    blkb = fm.Relu2MLP(W1, W2, margin=MARGIN, amax_init=1.0, fp8_up=True, keep_post=False)
+    ws_b8 = torch.empty(max(1, fm.lib().mlp_relu2_fwd_fp8up_workspace(M, D, H)), dtype=torch.uint8, device=dev)
+    blkb.forward(X, post_q=post_q, Y=Y, workspace=ws_b8)
+
+    def stepb():
+        blkb.forward(X, post_q=post_q, Y=Y, workspace=ws_b8)
+        blkb.backward(dY, X, None, dX, dW1, dW2, workspace=ws_b, post_q=post_q)
+        blkb.refresh_caches(workspace=ws_c)
+
+    t_sb = timed(stepb)
+    out["fp8up_fp8post_step_ms"] = round(t_sb, 4)
+    out["fp8up_fp8post_step_tflops"] = round(6 * mdh2 / (t_sb * 1e-3) / 1e12, 1)
+    out["fp8up_fp8post_step_pct_mixed_mfma_peak"] = round(100.0 * mixed_floor_us(M, D, H, 2) / (t_sb * 1e3), 2)
+    del blkb, ws_b8
 
     # layer-stack workload: 12 layers x 8 SGD steps at M=65536 (state carry per layer)
     from fp8_relu_mlp_amd.stack import Relu2Stack

@@ -7,7 +7,7 @@ PyTorch supplies device memory and streams and nothing else.  If the library
 is not built, the first call raises.
 
 Entry points (same names as the C ABI):
-  mlp_relu2_fwd, mlp_relu2_fwd_fp8up, mlp_relu2_bwd, fp8_cast_transpose, fp8_cast_transpose_w2,
+  mlp_relu2_fwd, mlp_relu2_fwd_fp8up, mlp_relu2_bwd, mlp_relu2_bwd_fp8post, fp8_cast_transpose, fp8_cast_transpose_w2,
   amax_reduce, fp8_scale_from_amax, fp8_linear, fp8_saturation_count, and the
   layer-stack helpers
   rmsnorm_fwd, rmsnorm_bwd, add_bf16, sgd_update_bf16
@@ -24,7 +24,7 @@ EVAL_BF16 = 1
 F32 = 0
 BF16 = 1
 
-__all__ = ["mlp_relu2_fwd", "mlp_relu2_fwd_fp8up", "mlp_relu2_bwd", "fp8_cast_transpose", "fp8_cast_transpose_w2", "amax_reduce",
+__all__ = ["mlp_relu2_fwd", "mlp_relu2_fwd_fp8up", "mlp_relu2_bwd", "mlp_relu2_bwd_fp8post", "fp8_cast_transpose", "fp8_cast_transpose_w2", "amax_reduce",
            "fp8_scale_from_amax", "fp8_linear", "fp8_saturation_count", "rmsnorm_fwd", "rmsnorm_bwd", "add_bf16", "sgd_update_bf16",
            "Relu2MLP", "KernelTimer", "Fp8MlpError", "TRAIN_FP8", "EVAL_BF16"]
 
@@ -91,6 +91,19 @@ def mlp_relu2_bwd(dY, X, W1, W2, post, dX, dW1, dW2, accumulate=False, workspace
     check("mlp_relu2_bwd", L.mlp_relu2_bwd(
         _p(dY), _p(X), _p(W1), _p(W2), _p(post), _p(dX), _p(dW1), _p(dW2), int(bool(accumulate)), M, d, h,
         _p(ws), wsb, _stream(stream)))
+
+
+def mlp_relu2_bwd_fp8post(dY, X, W1, W2, post_q, post_scale, dX, dW1, dW2, accumulate=False, workspace=None,
+                          stream=None):
+    """See mlp_relu2_bwd_fp8post in include/fp8mlp.h: the backward from the
+    e4m3 post copy post_q [M,h] (uint8) and the scale its forward used."""
+    M, d = X.shape
+    h = W1.shape[0]
+    L = lib()
+    ws, wsb = _ws(L.mlp_relu2_bwd_workspace(M, d, h), workspace, X.device)
+    check("mlp_relu2_bwd_fp8post", L.mlp_relu2_bwd_fp8post(
+        _p(dY), _p(X), _p(W1), _p(W2), _p(post_q), _p(post_scale), _p(dX), _p(dW1), _p(dW2), int(bool(accumulate)),
+        M, d, h, _p(ws), wsb, _stream(stream)))
 
 
 def fp8_cast_transpose(W, Wt_q, scale_in=None, scale_out=None, inv_scale_out=None, amax_out=None,
@@ -256,10 +269,16 @@ class Relu2MLP:
     casts W2 with the scale of the previous refresh's max|W2| times
     ``w2_margin`` instead of the exact max|W2| of the weights being cast (the
     first refresh is exact).
+
+    With ``keep_post=False`` the training forward writes only the e4m3 copy
+    of post (no bf16 post) and ``backward`` must be given that copy
+    (``post_q``); it then runs mlp_relu2_bwd_fp8post with the scale of the
+    last forward (``scale_used``), so the backward has to follow its own
+    forward before the next one.
     """
 
     def __init__(self, W1, W2, margin=2.0, amax_init=None, fp8_up=False, x_amax_init=None, amax_window=1,
-                 w2_scale="exact", w2_margin=1.0):
+                 w2_scale="exact", w2_margin=1.0, keep_post=True):
         dev = W1.device
         self.W1, self.W2, self.margin = W1, W2, float(margin)
         h, d = W1.shape
@@ -270,6 +289,7 @@ class Relu2MLP:
         if w2_scale not in ("exact", "delayed"):
             raise ValueError("w2_scale is 'exact' or 'delayed'")
         self.amax_window, self.w2_policy, self.w2_margin = int(amax_window), w2_scale, float(w2_margin)
+        self.keep_post = bool(keep_post)
         # rolling window: the last L measured amaxes, written in turn
         self.amax_hist = torch.zeros(self.amax_window, dtype=torch.float32, device=dev)
         self._hist_pos = 0
@@ -316,7 +336,10 @@ class Relu2MLP:
         x_amax_prev)."""
         M = X.shape[0]
         dev = X.device
-        post = torch.empty((M, self.h), dtype=torch.bfloat16, device=dev) if post is None else post
+        if mode == TRAIN_FP8 and not self.keep_post:
+            post = None
+        elif post is None:
+            post = torch.empty((M, self.h), dtype=torch.bfloat16, device=dev)
         if mode == TRAIN_FP8 and post_q is None:
             post_q = torch.empty((M, self.h), dtype=torch.uint8, device=dev)
         Y = torch.empty((M, self.d), dtype=torch.bfloat16, device=dev) if Y is None else Y
@@ -347,10 +370,20 @@ class Relu2MLP:
         """The amax measured by the most recent carried forward."""
         return self.amax_last_measured if self.amax_window > 1 else self.amax_prev
 
-    def backward(self, dY, X, post, dX=None, dW1=None, dW2=None, accumulate=False, workspace=None, stream=None):
+    def backward(self, dY, X, post, dX=None, dW1=None, dW2=None, accumulate=False, workspace=None, stream=None,
+                 post_q=None, post_scale=None):
+        """From the bf16 post, or (post None) from the e4m3 copy post_q and
+        the scale its forward used (default: this block's last scale)."""
         dev = X.device
         dX = torch.empty_like(X) if dX is None else dX
         dW1 = torch.empty((self.h, self.d), dtype=torch.float32, device=dev) if dW1 is None else dW1
         dW2 = torch.empty((self.d, self.h), dtype=torch.float32, device=dev) if dW2 is None else dW2
-        mlp_relu2_bwd(dY, X, self.W1, self.W2, post, dX, dW1, dW2, accumulate, workspace=workspace, stream=stream)
+        if post is not None:
+            mlp_relu2_bwd(dY, X, self.W1, self.W2, post, dX, dW1, dW2, accumulate, workspace=workspace,
+                          stream=stream)
+        else:
+            if post_q is None:
+                raise ValueError("backward needs post or post_q")
+            mlp_relu2_bwd_fp8post(dY, X, self.W1, self.W2, post_q, self.scale_used if post_scale is None else post_scale,
+                                  dX, dW1, dW2, accumulate, workspace=workspace, stream=stream)
         return dX, dW1, dW2

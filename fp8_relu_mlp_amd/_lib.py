@@ -31,6 +31,8 @@ SIGNATURES = {
                                     c_i64, c_i64, c_i64, vp, c_size, vp]),
     "mlp_relu2_bwd_workspace": (c_size, [c_i64, c_i64, c_i64]),
     "mlp_relu2_bwd": (c_int, [vp, vp, vp, vp, vp, vp, vp, vp, c_int, c_i64, c_i64, c_i64, vp, c_size, vp]),
+    "mlp_relu2_bwd_fp8post": (c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, c_int, c_i64, c_i64, c_i64, vp, c_size,
+                                      vp]),
     "fp8_cast_transpose_workspace": (c_size, [c_i64, c_i64]),
     "fp8_cast_transpose": (c_int, [vp, c_i64, c_i64, vp, vp, vp, vp, vp, vp, c_size, vp]),
     "fp8_cast_transpose_w2": (c_int, [vp, c_i64, c_i64, vp, vp, vp, vp, vp, c_size, vp]),

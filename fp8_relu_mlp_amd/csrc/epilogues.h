@@ -123,7 +123,7 @@ __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
 // dequantised: pre = fp32(fp32(acc * fp32(1 / *x_scale)) * *w_inv).
 template <bool DEQ>
 struct EpiRelu2QuantT {
-  uint16_t* post;
+  uint16_t* post;         // nullptr: only the quantised copy is kept
   uint8_t* post_q;        // nullptr: no quantised copy (eval)
   float* partial;         // [tiles_m * tiles_n]
   const float* amax_prev;
@@ -193,7 +193,9 @@ struct EpiRelu2QuantT {
     const float tile_max = __uint_as_float(m4 << 16);
     if (interior) {
       // interior tile: 32-bit offsets from the tile origin, no bounds checks
-      const __amdgpu_buffer_rsrc_t rp = make_rsrc(post + c.m0 * ld + c.n0, (uint64_t)C::BM * ld * 2);
+      const bool keep = post != nullptr;
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(keep ? (const void*)(post + c.m0 * ld + c.n0) : (const void*)post_q,
+                                                  keep ? (uint64_t)C::BM * ld * 2 : 0);
       // byte offsets of this thread's chunk in pass 0 and the per-pass step
       const uint32_t op = (uint32_t)T::row0() * (uint32_t)ld * 2 + T::chunk0() * 16;
       const uint32_t oq = (uint32_t)T::row0() * (uint32_t)ld + T::chunk0() * 8;
@@ -208,7 +210,7 @@ struct EpiRelu2QuantT {
         // (NaN and inf fail the test and take the general encode).
         if (tile_max * s <= 464.0f) {
           T::rows_interior(smem, [&](int p, uint4 v) {
-            buffer_store_stream16(rp, op + p * sp, v);
+            if (keep) buffer_store_stream16(rp, op + p * sp, v);
             uint2 q;
             q.x = pack_e4m3x4_inrange(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
             q.y = pack_e4m3x4_inrange(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
@@ -216,7 +218,7 @@ struct EpiRelu2QuantT {
           });
         } else {
           T::rows_interior(smem, [&](int p, uint4 v) {
-            buffer_store_stream16(rp, op + p * sp, v);
+            if (keep) buffer_store_stream16(rp, op + p * sp, v);
             uint2 q;
             q.x = pack_e4m3x4_nonneg(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
             q.y = pack_e4m3x4_nonneg(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
@@ -226,7 +228,7 @@ struct EpiRelu2QuantT {
       }
     } else {
       T::rows(smem, c, [&](int64_t m, int64_t n, uint4 v) {
-        store_stream(post + m * ld + n, v);
+        if (post) store_stream(post + m * ld + n, v);
         if (post_q) {
           uint2 q;
           q.x = pack_e4m3x4_nonneg(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
@@ -334,41 +336,141 @@ struct EpiDpre {
   }
 };
 
+// LDS image of a BM x BN tile of e4m3 codes: rows of BN/16 chunks of 16
+// bytes, the chunk index XOR-ed with the row's low bits (16 consecutive rows,
+// one chunk: 16 distinct bank groups).
+template <class C>
+struct Tile8 {
+  static constexpr int CPR = C::BN / 16;
+  static constexpr int XM = CPR < 16 ? CPR - 1 : 15;
+  static constexpr int BYTES = C::BM * C::BN;
+  static constexpr int PASSES = C::BM * CPR / C::NT;
+  static_assert((C::BM * CPR) % C::NT == 0, "row-order passes");
+  __device__ static __forceinline__ uint32_t off(int row, int chunk) {
+    return (uint32_t)(row * CPR + (chunk ^ (row & XM))) * 16u;
+  }
+  // Global e4m3 matrix (leading dimension ld bytes) -> LDS image, straight
+  // into LDS (streaming); rows past the matrix end read as zero.
+  __device__ static __forceinline__ void load(FP8MLP_LDS char* s, const TileCtx& c, const uint8_t* g, int64_t ld) {
+    const uint8_t* base = g + c.m0 * ld + c.n0;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (uint64_t)((c.M - c.m0) * ld - c.n0));
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int p = 0; p < PASSES; p++) {
+      const int i = (p * C::NW + wave) * 64 + c.lane;
+      const int row = i / CPR, ch = (i % CPR) ^ (row & XM);
+      buffer_load_lds16_stream(r, s + (p * C::NW + wave) * 1024, (uint32_t)(row * ld + ch * 16));
+    }
+  }
+};
+
+// Backward dgrad epilogue on the e4m3 copy of post (the bf16 post is not
+// kept: "A Retrospective on Our World Records", Main Track, the
+// implementation-note bullet on the BF16 post staying materialised and the
+// separate submission that drops it):
+//   post_hat = fp32(dec(post_q) * fp32(1 / *post_scale))
+//   dpre     = bf16(2 * sqrt(post_hat) * dpost),  dpost = the accumulator
+// The code tile comes into LDS in row order; each lane reads the 16 codes of
+// a fragment with one 16-byte read, keeps its dpre values in registers until
+// every wave has read its codes, then the bf16 tile is staged over the same
+// LDS and leaves in row order.
+struct EpiDpreQ {
+  const uint8_t* post_q;
+  const float* post_scale;
+  uint16_t* dpre;
+  int64_t ld;  // h
+
+  template <class C>
+  static constexpr int lds_bytes() { return Tile16<C>::BYTES > Tile8<C>::BYTES ? Tile16<C>::BYTES : Tile8<C>::BYTES; }
+
+  template <class C>
+  __device__ __forceinline__ void run(const TileCtx& c, f32x16 (&acc)[C::FM][C::FN], FP8MLP_LDS char* smem) {
+    static_assert(C::PERM, "needs 16 consecutive columns per lane");
+    using T = Tile16<C>;
+    using T8 = Tile8<C>;
+    const float inv = 1.0f / *post_scale;
+    __syncthreads();
+    T8::load(smem, c, post_q, ld);
+    wait_vmcnt<0>();
+    __syncthreads();
+    uint32_t o[C::FM][C::FN][8];
+#pragma unroll
+    for (int fm = 0; fm < C::FM; fm++) {
+      const int row = T::frag_row(c, fm);
+#pragma unroll
+      for (int fn = 0; fn < C::FN; fn++) {
+        // this lane's 16 columns start at a multiple of 16
+        const i32x4 q = lds_read_b128(smem, T8::off(row, T::frag_chunk(c, fn) / 2));
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(q[w], false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(q[w], true);
+          const float p[4] = {lo.x * inv, lo.y * inv, hi.x * inv, hi.y * inv};
+#pragma unroll
+          for (int i = 0; i < 2; i++) {
+            const int e = 4 * w + 2 * i;
+            // v_sqrt_f32 (within 1 ulp of fp32) is far below the bf16 rounding of dpre
+            const float r0 = __builtin_amdgcn_sqrtf(p[2 * i]), r1 = __builtin_amdgcn_sqrtf(p[2 * i + 1]);
+            o[fm][fn][e / 2] = pack_bf16x2((2.0f * r0) * acc[fm][fn][e], (2.0f * r1) * acc[fm][fn][e + 1]);
+          }
+        }
+      }
+    }
+    __syncthreads();   // every wave has read its codes: the bf16 image may overwrite them
+#pragma unroll
+    for (int fm = 0; fm < C::FM; fm++)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; fn++) T::put(smem, c, fm, fn, o[fm][fn]);
+    __syncthreads();
+    T::store(smem, c, dpre, ld);
+  }
+};
+
 // fp32 output: either the final weight gradient (optionally added to what is
-// there) or one split-k partial, written to out + split * split_stride.
+// there) or one split-k partial, written to out + split * split_stride.  With
+// div_by, every value is first multiplied by fp32(1 / *div_by) (the e4m3
+// post copy's scale when the GEMM ran on its codes).
 struct EpiF32 {
   float* out;
   int64_t ld;
   int64_t split_stride;   // elements between split partials (0: single split)
   int accumulate;         // add into out (single split only)
+  const float* div_by = nullptr;
 
   template <class C>
   static constexpr int lds_bytes() { return 0; }
 
   template <class C>
   __device__ __forceinline__ void run(const TileCtx& c, f32x16 (&acc)[C::FM][C::FN], FP8MLP_LDS char*) {
-    static_assert(C::PERM, "needs 16 consecutive columns per lane");
+    // four runs of four consecutive columns per lane and fragment in either
+    // layout (PERM: one run of 16); h and d are multiples of 32, so a
+    // fragment is wholly inside or outside the matrix
     float* base = out + (int64_t)c.split * split_stride;
+    const float f = div_by ? 1.0f / *div_by : 1.0f;
 #pragma unroll
     for (int fm = 0; fm < C::FM; fm++) {
       const int64_t m = c.m0 + epi_row<C>(c, fm);
       if (m >= c.M) continue;
 #pragma unroll
       for (int fn = 0; fn < C::FN; fn++) {
-        const int64_t n = c.n0 + epi_col<C>(c, fn, 0);
-        if (n >= c.N) continue;
-        float4* dst = (float4*)(base + m * ld + n);
+        if (c.n0 + epi_col<C>(c, fn, 0) >= c.N) continue;
 #pragma unroll
         for (int g = 0; g < 4; g++) {
+          float4* dst = (float4*)(base + m * ld + c.n0 + epi_col<C>(c, fn, 4 * g));
           float4 v = {acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2], acc[fm][fn][4 * g + 3]};
+          if (div_by) {
+            v.x *= f;
+            v.y *= f;
+            v.z *= f;
+            v.w *= f;
+          }
           if (accumulate) {
-            const float4 o = dst[g];
+            const float4 o = *dst;
             v.x += o.x;
             v.y += o.y;
             v.z += o.z;
             v.w += o.w;
           }
-          dst[g] = v;
+          *dst = v;
         }
       }
     }

@@ -40,9 +40,15 @@ enum { KC = 0, MNC = 1 };
 // symbol, which profilers report per symbol.
 enum : int { KID_UP = 1, KID_DOWN8, KID_DOWN_BF16, KID_DPOST, KID_DX, KID_DW1, KID_DW2, KID_LINEAR, KID_UP8 };
 
-template <int ELT_, int BM_, int BN_, int RB_, int STAGES_, int OCC_, int QL_, int PL_, int REG_ = 0, int NW_ = 4>
+template <int ELT_, int BM_, int BN_, int RB_, int STAGES_, int OCC_, int QL_, int PL_, int REG_ = 0, int NW_ = 4,
+          int PELT_ = 0>
 struct GemmCfg {
   static constexpr int ELT = ELT_;                 // bytes per element: 2 bf16, 1 e4m3
+  // bytes per element of the P operand in memory and LDS (default ELT).
+  // PELT == 1 with ELT == 2: an e4m3 P operand under the bf16 MFMA, widened
+  // to bf16 exactly (every e4m3 value is a bf16 value) as its fragments are
+  // read; row-contiguous only.
+  static constexpr int PELT = PELT_ ? PELT_ : ELT_;
   // REG == 1: tiles go global -> VGPRs -> LDS (buffer_load_dwordx4 +
   // ds_write_b128), the next tile waiting in registers while the current one
   // is computed; REG == 0: global -> LDS directly (buffer_load ... lds) with
@@ -64,7 +70,7 @@ struct GemmCfg {
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int KSTEP = ELT == 2 ? 32 : 64; // bytes of k per MFMA
   static constexpr int SL = RB / KSTEP;            // MFMA k-steps per tile
-  static constexpr int Q_BYTES = BM * RB, P_BYTES = BN * RB;
+  static constexpr int Q_BYTES = BM * RB, P_BYTES = BN * BK * PELT;
   static constexpr int STAGE_BYTES = Q_BYTES + P_BYTES;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int Q_LOADS = Q_BYTES / (1024 * NW);   // 16 B x 64 lanes x NW waves per round
@@ -72,7 +78,9 @@ struct GemmCfg {
   static constexpr int LOADS = Q_LOADS + P_LOADS;
   // the P operand's row order gives each lane 16 consecutive n, except for
   // transposed fp8 reads, which give 4 runs of 4
-  static constexpr bool PERM = !(ELT == 1 && PL == MNC);
+  static constexpr bool PERM = !((ELT == 1 || PELT == 1) && PL == MNC);
+  static_assert(PELT == ELT || (ELT == 2 && PELT == 1 && PL == MNC && REG == 0),
+                "e4m3 P under the bf16 MFMA: row-contiguous, loaded straight into LDS");
   static_assert(RB == 64 || RB == 128, "row bytes");
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
   static_assert(NW == 4 || NW == 8, "waves");
@@ -81,7 +89,7 @@ struct GemmCfg {
   static_assert(NW == 4 || (REG == 0 && STAGES == 2 && OCC == 1), "the two-group kernel: direct loads, two buffers");
   // the row-contiguous swizzle XORs bits 6-7 (bf16) or 4-6 (e4m3) of the byte offset
   static_assert(QL == KC || (BM * ELT) % (ELT == 2 ? 256 : 128) == 0, "row-contiguous Q tile rows");
-  static_assert(PL == KC || (BN * ELT) % (ELT == 2 ? 256 : 128) == 0, "row-contiguous P tile rows");
+  static_assert(PL == KC || (BN * PELT) % (PELT == 2 ? 256 : 128) == 0, "row-contiguous P tile rows");
   static_assert(LDS_BYTES * OCC <= 160 * 1024, "LDS");
   static_assert(LOADS * (STAGES - 2) < 64, "vmcnt");
   static_assert(REG == 0 || (REG == 1 && STAGES == 2), "register staging: two LDS buffers, one register set");
@@ -169,6 +177,19 @@ struct FragT<1> {
   using type = i32x8;      // 32 e4m3 of k per lane (32x32x64 MFMA operand)
 };
 
+// 8 e4m3 codes (byte i = k + i) -> the same 8 values as bf16, exactly: the
+// converter gives fp32, whose upper half is the bf16 pattern (an e4m3 value
+// has at most 4 significant bits).
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(i32x2 c) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(c[0], false), b = __builtin_amdgcn_cvt_pk_f32_fp8(c[0], true);
+  const f32x2 e = __builtin_amdgcn_cvt_pk_f32_fp8(c[1], false), f = __builtin_amdgcn_cvt_pk_f32_fp8(c[1], true);
+  const auto hi2 = [](float x, float y) {
+    return (int)__builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
+  };
+  const i32x4 v = {hi2(a.x, a.y), hi2(b.x, b.y), hi2(e.x, e.y), hi2(f.x, f.y)};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
 // Two transposed 4 x bf16 reads (k .. k+3, k+4 .. k+7) -> one 8 x bf16 operand.
 __device__ __forceinline__ bf16x8_t tr16_pair(i16x4 lo, i16x4 hi) {
   const i32x4 v = {(int)((uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16)),
@@ -247,14 +268,15 @@ __device__ __forceinline__ void sched_mix() {
 // memory relative to the tile origin (at k = 0 of this block's range).
 template <class C, int L, int ROWS, bool IS_P>
 __device__ __forceinline__ uint32_t load_off(int c, int64_t ld_bytes) {
+  constexpr int E = IS_P ? C::PELT : C::ELT;
   if constexpr (L == KC) {
     const int row = c / C::CPR, pc = c % C::CPR;
     const int lc = pc ^ (IS_P ? swz_rows_p<C::CPR>(row) : swz_rows_q<C::CPR>(row));
     return (uint32_t)(row * ld_bytes + lc * 16);
   } else {
-    constexpr int MCPR = ROWS * C::ELT / 16;   // chunks per LDS row (one k)
+    constexpr int MCPR = ROWS * E / 16;   // chunks per LDS row (one k)
     const int k = c / MCPR, pc = c % MCPR;
-    const int lc = ((pc * 16) ^ swz_mn<C::ELT>(k)) / 16;
+    const int lc = ((pc * 16) ^ swz_mn<E>(k)) / 16;
     return (uint32_t)(k * ld_bytes + lc * 16);
   }
 }
@@ -302,7 +324,7 @@ struct TileLoads {
   uint32_t qstep, pstep;   // bytes between consecutive k-tiles
 
   __device__ __forceinline__ void init(const GemmArgs& a, const TilePos& t, int wave, int lane) {
-    const int64_t ldq_b = a.ldq * C::ELT, ldp_b = a.ldp * C::ELT;
+    const int64_t ldq_b = a.ldq * C::ELT, ldp_b = a.ldp * C::PELT;
     const char* q = (const char*)a.q;
     const char* p = (const char*)a.p;
     if constexpr (C::QL == KC) {
@@ -311,9 +333,9 @@ struct TileLoads {
       rq = make_rsrc(q + t.kb * ldq_b + t.m0 * C::ELT, (uint64_t)((t.ke - t.kb) * ldq_b - t.m0 * C::ELT));
     }
     if constexpr (C::PL == KC) {
-      rp = make_rsrc(p + t.n0 * ldp_b + t.kb * C::ELT, (uint64_t)((a.N - t.n0) * ldp_b - t.kb * C::ELT));
+      rp = make_rsrc(p + t.n0 * ldp_b + t.kb * C::PELT, (uint64_t)((a.N - t.n0) * ldp_b - t.kb * C::PELT));
     } else {
-      rp = make_rsrc(p + t.kb * ldp_b + t.n0 * C::ELT, (uint64_t)((t.ke - t.kb) * ldp_b - t.n0 * C::ELT));
+      rp = make_rsrc(p + t.kb * ldp_b + t.n0 * C::PELT, (uint64_t)((t.ke - t.kb) * ldp_b - t.n0 * C::PELT));
     }
 #pragma unroll
     for (int j = 0; j < C::Q_LOADS; j++)
@@ -365,6 +387,13 @@ struct FragReader {
       const int r = wn * C::WTN + (C::PERM ? perm_p(lane & 31) : (lane & 31));
       prow_off = r * C::RB;
       px = swz_rows_p<C::CPR>(r);
+    } else if constexpr (C::ELT == 2 && C::PELT == 1) {
+      // one transposed e4m3 read gives this lane k = 8h .. 8h+7 of one column,
+      // the bf16 operand's k range; the columns follow the e4m3 order below
+      const int kq = (lane & 15) >> 1;
+      const int nb = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+      prow_off = (8 * h + kq) * C::BN;
+      px = wn * C::WTN + nb;
     } else if constexpr (C::ELT == 2) {
       const int kq = (lane & 15) >> 2;
       const int q4 = lane & 3;
@@ -380,7 +409,7 @@ struct FragReader {
   }
   // LDS reads per fragment
   static constexpr int QR = C::QL == KC ? (C::ELT == 2 ? 1 : 2) : (C::ELT == 2 ? 2 : 4);
-  static constexpr int PR = C::PL == KC ? (C::ELT == 2 ? 1 : 2) : (C::ELT == 2 ? 2 : 4);
+  static constexpr int PR = C::PL == KC ? (C::ELT == 2 ? 1 : 2) : (C::ELT == 2 ? (C::PELT == 2 ? 2 : 1) : 4);
 
   __device__ __forceinline__ Frag q(const FP8MLP_LDS char* sq, int s, int fm) const {
     if constexpr (C::ELT == 2) {
@@ -401,7 +430,11 @@ struct FragReader {
     }
   }
   __device__ __forceinline__ Frag p(const FP8MLP_LDS char* sp, int s, int fn) const {
-    if constexpr (C::ELT == 2) {
+    if constexpr (C::ELT == 2 && C::PELT == 1) {
+      const int kq = (lane & 15) >> 1;
+      const uint32_t col = (uint32_t)((px + fn * 32) ^ ((kq & 7) << 4));
+      return e4m3x8_to_bf16x8(lds_read_tr8(sp, prow_off + (16 * s) * C::BN + col));
+    } else if constexpr (C::ELT == 2) {
       if constexpr (C::PL == KC) {
         const uint32_t off = prow_off + fn * 32 * C::RB + (((2 * s + h) ^ px) * 16);
         return __builtin_bit_cast(bf16x8_t, lds_read_b128(sp, off));

@@ -3,6 +3,10 @@
 //   dX    = dpre W1          bf16 out
 //   dW1   = dpre^T X         fp32, split-k over M, reduced in split order
 //   dW2   = dY^T post        fp32, split-k over M, reduced in split order
+// mlp_relu2_bwd_fp8post: the same backward when only the e4m3 copy of post
+// was kept; post_hat = dec(post_q) / scale takes post's place, the dgrad
+// epilogue decodes the codes and dW2 runs on them directly (e4m3 widened to
+// bf16 as its fragments are read, the 1/scale applied to the fp32 result).
 // W1 and W2 are first transposed into the workspace (4.7 MB each at the
 // GPT-2-small shape) so that both dgrad GEMMs read k-contiguous operands
 // with plain 16-byte LDS reads.
@@ -18,6 +22,8 @@ using CfgDx = GemmCfg<2, 192, 256, 128, 2, 1, KC, KC, 0, 8>;
 // dpre^T . X and dY^T . post: both operands are row-contiguous with k = token;
 // 256 x 256 tiles, two groups of four waves.
 using CfgDw = GemmCfg<2, 256, 256, 128, 2, 1, MNC, MNC, 0, 8>;
+// dY^T . dec(post_q): the same tiles with the e4m3 codes as the P operand.
+using CfgDw2q = GemmCfg<2, 256, 256, 128, 2, 1, MNC, MNC, 0, 8, 1>;
 
 struct BwdPlan {
   size_t dpre_bytes, wt_bytes, part_bytes;   // dpre; W1t + W2t; split-k partials of dW
@@ -129,19 +135,81 @@ static int launch_zero(float* out, int64_t n, hipStream_t st) {
   return launch_status();
 }
 
-// One weight gradient C [Mo, No] = A^T B with A [K, Mo], B [K, No] (K = tokens).
-template <int KID>
-static int weight_grad(const uint16_t* A, int64_t Mo, const uint16_t* B, int64_t No, int64_t K, float* out,
-                       int accumulate, const BwdPlan& plan, float* part, hipStream_t st) {
-  GemmArgs a{A, Mo, B, No, Mo, No, K, (int)cdiv(Mo, CfgDw::BM), (int)cdiv(No, CfgDw::BN), plan.splits,
-             plan.k_per_split};
+// One weight gradient C [Mo, No] = A^T B with A [K, Mo], B [K, No] (K = tokens),
+// optionally times fp32(1 / *div_by).
+template <class C, int KID>
+static int weight_grad(const uint16_t* A, int64_t Mo, const void* B, int64_t No, int64_t K, float* out,
+                       int accumulate, const BwdPlan& plan, float* part, hipStream_t st,
+                       const float* div_by = nullptr) {
+  static_assert(C::BM == CfgDw::BM && C::BN == CfgDw::BN, "the plan's split count assumes these tiles");
+  GemmArgs a{A, Mo, B, No, Mo, No, K, (int)cdiv(Mo, C::BM), (int)cdiv(No, C::BN), plan.splits, plan.k_per_split};
   if (plan.splits == 1) {
-    EpiF32 epi{out, No, 0, accumulate};
-    return launch_gemm<CfgDw, KID>(a, epi, st);
+    EpiF32 epi{out, No, 0, accumulate, div_by};
+    return launch_gemm<C, KID>(a, epi, st);
   }
-  EpiF32 epi{part, No, Mo * No, 0};
-  FP8MLP_TRY(launch_gemm<CfgDw, KID>(a, epi, st));
+  EpiF32 epi{part, No, Mo * No, 0, div_by};
+  FP8MLP_TRY(launch_gemm<C, KID>(a, epi, st));
   return launch_reduce(part, plan.splits, Mo * No, out, accumulate, st);
+}
+
+// The two entry points differ in the dgrad epilogue and the dW2 operand.
+template <bool Q>
+static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* W1, const uint16_t* W2,
+                        const void* post, const float* post_scale, uint16_t* dX, float* dW1, float* dW2,
+                        int accumulate, int64_t M, int64_t d, int64_t h, void* workspace, size_t workspace_bytes,
+                        hipStream_t st) {
+  FP8MLP_REQUIRE(M >= 0 && d > 0 && h > 0 && d % 64 == 0 && h % 64 == 0, FP8MLP_E_SHAPE);
+  FP8MLP_REQUIRE(accumulate == 0 || accumulate == 1, FP8MLP_E_ARG);
+  FP8MLP_REQUIRE(dW1 && dW2, FP8MLP_E_NULL);
+  if (M > 0) FP8MLP_REQUIRE(dY && X && W1 && W2 && post && dX && (!Q || post_scale), FP8MLP_E_NULL);
+  for (const void* p : {(const void*)dY, (const void*)X, (const void*)W1, (const void*)W2, (const void*)post,
+                        (const void*)dX, (const void*)dW1, (const void*)dW2})
+    FP8MLP_REQUIRE(p == nullptr || aligned16(p), FP8MLP_E_ALIGN);
+  FP8MLP_REQUIRE(((uintptr_t)post_scale & 3) == 0, FP8MLP_E_ALIGN);
+  const BwdPlan plan = bwd_plan(M, d, h);
+  const size_t need = plan.dpre_bytes + plan.wt_bytes + plan.part_bytes;
+  FP8MLP_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), FP8MLP_E_WORKSPACE);
+  FP8MLP_REQUIRE(need == 0 || aligned16(workspace), FP8MLP_E_ALIGN);
+  FP8MLP_TRY(check_device());
+
+  if (M == 0) {
+    if (!accumulate) {
+      FP8MLP_TRY(launch_zero(dW1, h * d, st));
+      FP8MLP_TRY(launch_zero(dW2, d * h, st));
+    }
+    return FP8MLP_OK;
+  }
+  uint16_t* dpre = (uint16_t*)workspace;
+  uint16_t* W1t = (uint16_t*)((char*)workspace + plan.dpre_bytes);                    // [d, h]
+  uint16_t* W2t = (uint16_t*)((char*)W1t + plan.wt_bytes / 2);                         // [h, d]
+  float* part = (float*)((char*)workspace + plan.dpre_bytes + plan.wt_bytes);
+
+  FP8MLP_TRY(launch_transpose_weights(W1, W2, d, h, W1t, W2t, st));
+  // 1. dpost = dY W2 with the sqrt(post) epilogue -> dpre
+  {
+    GemmArgs a{dY, d, W2t, d, M, h, d, (int)cdiv(M, CfgDpost::BM), (int)cdiv(h, CfgDpost::BN), 1, d};
+    if constexpr (Q) {
+      EpiDpreQ epi{(const uint8_t*)post, post_scale, dpre, h};
+      FP8MLP_TRY(launch_gemm<CfgDpost, KID_DPOST>(a, epi, st));
+    } else {
+      EpiDpre epi{(const uint16_t*)post, dpre, h};
+      FP8MLP_TRY(launch_gemm<CfgDpost, KID_DPOST>(a, epi, st));
+    }
+  }
+  // 2. dX = dpre W1
+  {
+    GemmArgs a{dpre, h, W1t, h, M, d, h, (int)cdiv(M, CfgDx::BM), (int)cdiv(d, CfgDx::BN), 1, h};
+    EpiBf16Out epi{dX, d, 0, nullptr, 0.0f, nullptr, nullptr};
+    FP8MLP_TRY(launch_gemm<CfgDx, KID_DX>(a, epi, st));
+  }
+  // 3. dW1 = dpre^T X ; 4. dW2 = dY^T post  (or (dY^T dec(post_q)) / scale)
+  FP8MLP_TRY((weight_grad<CfgDw, KID_DW1>(dpre, h, X, d, M, dW1, accumulate, plan, part, st)));
+  if constexpr (Q) {
+    FP8MLP_TRY((weight_grad<CfgDw2q, KID_DW2>(dY, d, post, h, M, dW2, accumulate, plan, part, st, post_scale)));
+  } else {
+    FP8MLP_TRY((weight_grad<CfgDw, KID_DW2>(dY, d, post, h, M, dW2, accumulate, plan, part, st)));
+  }
+  return FP8MLP_OK;
 }
 
 }  // namespace fp8mlp
@@ -159,49 +227,16 @@ size_t mlp_relu2_bwd_workspace(int64_t M, int64_t d, int64_t h) {
 int mlp_relu2_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* W1, const uint16_t* W2,
                   const uint16_t* post, uint16_t* dX, float* dW1, float* dW2, int accumulate, int64_t M,
                   int64_t d, int64_t h, void* workspace, size_t workspace_bytes, void* stream) {
-  FP8MLP_REQUIRE(M >= 0 && d > 0 && h > 0 && d % 64 == 0 && h % 64 == 0, FP8MLP_E_SHAPE);
-  FP8MLP_REQUIRE(accumulate == 0 || accumulate == 1, FP8MLP_E_ARG);
-  FP8MLP_REQUIRE(dW1 && dW2, FP8MLP_E_NULL);
-  if (M > 0) FP8MLP_REQUIRE(dY && X && W1 && W2 && post && dX, FP8MLP_E_NULL);
-  for (const void* p : {(const void*)dY, (const void*)X, (const void*)W1, (const void*)W2, (const void*)post,
-                        (const void*)dX, (const void*)dW1, (const void*)dW2})
-    FP8MLP_REQUIRE(p == nullptr || aligned16(p), FP8MLP_E_ALIGN);
-  const BwdPlan plan = bwd_plan(M, d, h);
-  const size_t need = plan.dpre_bytes + plan.wt_bytes + plan.part_bytes;
-  FP8MLP_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), FP8MLP_E_WORKSPACE);
-  FP8MLP_REQUIRE(need == 0 || aligned16(workspace), FP8MLP_E_ALIGN);
-  FP8MLP_TRY(check_device());
+  return mlp_bwd_impl<false>(dY, X, W1, W2, post, nullptr, dX, dW1, dW2, accumulate, M, d, h, workspace,
+                             workspace_bytes, (hipStream_t)stream);
+}
 
-  hipStream_t st = (hipStream_t)stream;
-  if (M == 0) {
-    if (!accumulate) {
-      FP8MLP_TRY(launch_zero(dW1, h * d, st));
-      FP8MLP_TRY(launch_zero(dW2, d * h, st));
-    }
-    return FP8MLP_OK;
-  }
-  uint16_t* dpre = (uint16_t*)workspace;
-  uint16_t* W1t = (uint16_t*)((char*)workspace + plan.dpre_bytes);                    // [d, h]
-  uint16_t* W2t = (uint16_t*)((char*)W1t + plan.wt_bytes / 2);                         // [h, d]
-  float* part = (float*)((char*)workspace + plan.dpre_bytes + plan.wt_bytes);
-
-  FP8MLP_TRY(launch_transpose_weights(W1, W2, d, h, W1t, W2t, st));
-  // 1. dpost = dY W2 with the sqrt(post) epilogue -> dpre
-  {
-    GemmArgs a{dY, d, W2t, d, M, h, d, (int)cdiv(M, CfgDpost::BM), (int)cdiv(h, CfgDpost::BN), 1, d};
-    EpiDpre epi{post, dpre, h};
-    FP8MLP_TRY(launch_gemm<CfgDpost, KID_DPOST>(a, epi, st));
-  }
-  // 2. dX = dpre W1
-  {
-    GemmArgs a{dpre, h, W1t, h, M, d, h, (int)cdiv(M, CfgDx::BM), (int)cdiv(d, CfgDx::BN), 1, h};
-    EpiBf16Out epi{dX, d, 0, nullptr, 0.0f, nullptr, nullptr};
-    FP8MLP_TRY(launch_gemm<CfgDx, KID_DX>(a, epi, st));
-  }
-  // 3. dW1 = dpre^T X ; 4. dW2 = dY^T post
-  FP8MLP_TRY(weight_grad<KID_DW1>(dpre, h, X, d, M, dW1, accumulate, plan, part, st));
-  FP8MLP_TRY(weight_grad<KID_DW2>(dY, d, post, h, M, dW2, accumulate, plan, part, st));
-  return FP8MLP_OK;
+int mlp_relu2_bwd_fp8post(const uint16_t* dY, const uint16_t* X, const uint16_t* W1, const uint16_t* W2,
+                          const uint8_t* post_q, const float* post_scale, uint16_t* dX, float* dW1, float* dW2,
+                          int accumulate, int64_t M, int64_t d, int64_t h, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return mlp_bwd_impl<true>(dY, X, W1, W2, post_q, post_scale, dX, dW1, dW2, accumulate, M, d, h, workspace,
+                            workspace_bytes, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -49,7 +49,7 @@ int mlp_relu2_fwd(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t
   FP8MLP_REQUIRE(M >= 0 && d > 0 && h > 0 && d % 64 == 0 && h % 64 == 0, FP8MLP_E_SHAPE);
   FP8MLP_REQUIRE(!train || h % 128 == 0, FP8MLP_E_SHAPE);
   FP8MLP_REQUIRE(amax_out != nullptr, FP8MLP_E_NULL);
-  if (M > 0) FP8MLP_REQUIRE(X && W1 && post && Y, FP8MLP_E_NULL);
+  if (M > 0) FP8MLP_REQUIRE(X && W1 && Y && (post || train), FP8MLP_E_NULL);
   if (train) {
     FP8MLP_REQUIRE(amax_prev != nullptr, FP8MLP_E_NULL);
     if (M > 0) FP8MLP_REQUIRE(W2t_q && w2_inv_scale && post_q, FP8MLP_E_NULL);
@@ -119,7 +119,7 @@ int mlp_relu2_fwd_fp8up(const uint16_t* X, const float* x_scale, const uint8_t* 
                         void* stream) {
   FP8MLP_REQUIRE(M >= 0 && d > 0 && h > 0 && d % 128 == 0 && h % 128 == 0, FP8MLP_E_SHAPE);
   FP8MLP_REQUIRE(x_scale && W1t_q && w1_inv_scale && W2t_q && w2_inv_scale && amax_prev && amax_out, FP8MLP_E_NULL);
-  if (M > 0) FP8MLP_REQUIRE(X && post && post_q && Y, FP8MLP_E_NULL);
+  if (M > 0) FP8MLP_REQUIRE(X && post_q && Y, FP8MLP_E_NULL);
   FP8MLP_REQUIRE(margin > 0.0f && margin <= 3.4e38f, FP8MLP_E_ARG);
   for (const void* p : {(const void*)X, (const void*)W1t_q, (const void*)W2t_q, (const void*)post,
                         (const void*)post_q, (const void*)Y})

@@ -34,7 +34,9 @@ W1 cache is refreshed after each update as well), ``amax_window`` and
 ``w2_scale`` / ``w2_margin`` (the scaling policies of ``Relu2MLP``).  With
 ``telemetry`` each layer's forward is followed by fp8_saturation_count on its
 e4m3 post copy; ``saturated`` [L] (int64, device) holds the counts of the
-last step and ``saturation_rate(l)`` their share of the M*h codes.
+last step and ``saturation_rate(l)`` their share of the M*h codes.  With
+``keep_post=False`` no layer keeps its bf16 post: each keeps its e4m3 copy,
+and the backward runs on it with the scale recorded in ``state``.
 """
 import numpy as np
 import torch
@@ -45,12 +47,13 @@ from . import (TRAIN_FP8, Relu2MLP, add_bf16, fp8_saturation_count, lib,
 
 class Relu2Stack:
     def __init__(self, W1s, W2s, margin=2.0, lr=1e-3, eps=1e-6, loss="mean", fp8_up=False, amax_window=1,
-                 w2_scale="exact", w2_margin=1.0, telemetry=False):
+                 w2_scale="exact", w2_margin=1.0, telemetry=False, keep_post=True):
         if len(W1s) != len(W2s) or not W1s:
             raise ValueError("need the same positive number of W1 and W2 tensors")
         self.layers = [Relu2MLP(w1, w2, margin=margin, amax_init=1.0, fp8_up=fp8_up, amax_window=amax_window,
-                                w2_scale=w2_scale, w2_margin=w2_margin) for w1, w2 in zip(W1s, W2s)]
-        self.fp8_up, self.telemetry = bool(fp8_up), bool(telemetry)
+                                w2_scale=w2_scale, w2_margin=w2_margin, keep_post=keep_post)
+                       for w1, w2 in zip(W1s, W2s)]
+        self.fp8_up, self.telemetry, self.keep_post = bool(fp8_up), bool(telemetry), bool(keep_post)
         self.L = len(self.layers)
         self.d, self.h = self.layers[0].d, self.layers[0].h
         if loss not in ("mean", "sum"):
@@ -68,8 +71,14 @@ class Relu2Stack:
         self.x = [torch.empty((M, d), dtype=bf, device=dev) for _ in range(L + 1)]
         self.xn = [torch.empty((M, d), dtype=bf, device=dev) for _ in range(L)]
         self.inv = [torch.empty((M,), dtype=f32, device=dev) for _ in range(L)]
-        self.post = [torch.empty((M, h), dtype=bf, device=dev) for _ in range(L)]
-        self.post_q = torch.empty((M, h), dtype=torch.uint8, device=dev)
+        if self.keep_post:
+            self.post = [torch.empty((M, h), dtype=bf, device=dev) for _ in range(L)]
+            self.post_q = torch.empty((M, h), dtype=torch.uint8, device=dev)
+            self.post_qs = None
+        else:
+            self.post = [None] * L
+            self.post_qs = [torch.empty((M, h), dtype=torch.uint8, device=dev) for _ in range(L)]
+            self.post_q = self.post_qs[0]
         self.Y = torch.empty((M, d), dtype=bf, device=dev)
         self.g = torch.empty((M, d), dtype=bf, device=dev)
         self.dxn = torch.empty((M, d), dtype=bf, device=dev)
@@ -103,6 +112,8 @@ class Relu2Stack:
         self._alloc(M, X.device)
         self.x[0].copy_(X)
         for l, blk in enumerate(self.layers):
+            if not self.keep_post:
+                self.post_q = self.post_qs[l]
             rmsnorm_fwd(self.x[l], self.xn[l], self.inv[l], self.eps)
             if self.steps_done == 0:
                 blk.forward(self.xn[l], post=self.post[l], post_q=self.post_q, Y=self.Y, workspace=self.ws_f)
@@ -121,7 +132,11 @@ class Relu2Stack:
             blk = self.layers[l]
             if observe:
                 self.g_in = self.g.clone()
-            blk.backward(self.g, self.xn[l], self.post[l], self.dxn, self.dW1, self.dW2, workspace=self.ws_b)
+            if self.keep_post:
+                blk.backward(self.g, self.xn[l], self.post[l], self.dxn, self.dW1, self.dW2, workspace=self.ws_b)
+            else:
+                blk.backward(self.g, self.xn[l], None, self.dxn, self.dW1, self.dW2, workspace=self.ws_b,
+                             post_q=self.post_qs[l], post_scale=self.state[l, 1:2])
             rmsnorm_bwd(self.x[l], self.inv[l], self.dxn, self.g, self.g)
             if observe:
                 observe(l, "bwd", self)
@@ -141,6 +156,8 @@ class Relu2Stack:
     def clip_fraction(self, l):
         """Share of layer l's last post values that the e4m3 copy saturated
         (post * scale > 448); a diagnostic read with PyTorch, not a step of
-        the method."""
+        the method (needs keep_post)."""
+        if not self.keep_post:
+            raise ValueError("clip_fraction reads the bf16 post; use telemetry with keep_post=False")
         s = self.layers[l].scale_used
         return float((self.post[l].float() * s > 448.0).float().mean().item())

@@ -83,6 +83,8 @@ int fp8mlp_last_hip_error(void);
  *   The scale depends only on amax_prev (the previous step's amax_out), so
  *   quantisation happens inside the up-projection epilogue and the forward
  *   never waits for the current amax.
+ * In TRAIN mode post may be NULL: then only post_q is written (the backward
+ * is mlp_relu2_bwd_fp8post).
  * EVAL (mode FP8MLP_EVAL_BF16), per "NanoGPT Speedrun (Track 1)", "Approach"
  *   item 5 (bf16 at eval): post as above, Y = bf16(post W2^T) with the bf16 W2;
  *   post_q, W2t_q, w2_inv_scale and amax_prev are not read (may be NULL);
@@ -128,6 +130,27 @@ size_t mlp_relu2_bwd_workspace(int64_t M, int64_t d, int64_t h);
 int mlp_relu2_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* W1, const uint16_t* W2,
                   const uint16_t* post, uint16_t* dX, float* dW1, float* dW2, int accumulate, int64_t M,
                   int64_t d, int64_t h, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * mlp_relu2_bwd_fp8post -- the backward when the forward kept only the e4m3
+ * copy of post (mlp_relu2_fwd / mlp_relu2_fwd_fp8up in TRAIN mode with post
+ * = NULL).  "A Retrospective on Our World Records", Main Track: the BF16 post
+ * stays materialised there by choice; dropping it, and rebuilding what the
+ * backward needs from the FP8 copy, is the orthogonal variant the page
+ * points to.  post's place is taken by
+ *   post_hat = fp32(dec(post_q) * fp32(1 / *post_scale))
+ *   dpre = bf16(2 * sqrt(post_hat) * dpost),  dpost = dY W2
+ *   dW2  = (dY^T dec(post_q)) * fp32(1 / *post_scale)   (fp32 accumulate)
+ *   dX, dW1 as in mlp_relu2_bwd.
+ * post_q [M, h] e4m3 and post_scale (device fp32: the scale_out of that
+ * forward) replace post; everything else, including the workspace
+ * (mlp_relu2_bwd_workspace), is as in mlp_relu2_bwd.
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_ARCH, E_ARG, E_HIP.
+ * ---------------------------------------------------------------------- */
+int mlp_relu2_bwd_fp8post(const uint16_t* dY, const uint16_t* X, const uint16_t* W1, const uint16_t* W2,
+                          const uint8_t* post_q, const float* post_scale, uint16_t* dX, float* dW1, float* dW2,
+                          int accumulate, int64_t M, int64_t d, int64_t h, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* ------------------------------------------------------------------------
  * fp8_cast_transpose -- bf16 weight W [N, K] -> e4m3 Wt_q [K, N] (the
@@ -229,7 +252,8 @@ int fp8_linear(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, con
  * 128; M >= 0.  workspace: mlp_relu2_fwd_fp8up_workspace(M, d, h) bytes
  * (the partial amax tensor, per-block maxima of |X| and the e4m3 copy of X;
  * 0 for M = 0).  The backward is
- * mlp_relu2_bwd with the bf16 W1 / W2 and the post written here.
+ * mlp_relu2_bwd with the bf16 W1 / W2 and the post written here (post may be
+ * NULL: then mlp_relu2_bwd_fp8post on post_q).
  * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_ARCH, E_ARG, E_HIP.
  * ---------------------------------------------------------------------- */
 size_t mlp_relu2_fwd_fp8up_workspace(int64_t M, int64_t d, int64_t h);

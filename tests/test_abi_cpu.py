@@ -132,3 +132,32 @@ def test_stack_helpers_validation(L):
     assert L.sgd_update_bf16(16, 16, 12, 1e-3, None) == E_SHAPE
     assert L.sgd_update_bf16(16, 16, 16, float("nan"), None) == E_ARG
     assert L.sgd_update_bf16(16, 40, 16, 1e-3, None) == E_ALIGN
+
+
+def test_variant_entry_points_validation(L):
+    """The e4m3 up-projection forward, the backward on the e4m3 post copy and
+    the top-code count reject bad arguments before touching a device."""
+    ws = L.mlp_relu2_fwd_fp8up_workspace(256, 128, 256)
+    assert ws >= 256 * 128 and L.mlp_relu2_fwd_fp8up_workspace(0, 128, 256) == 0
+    args = [16, 16, 16, 16, 16, 16, 16, 2.0, 16, 16, 16, 16, 16, 16]
+    assert L.mlp_relu2_fwd_fp8up(*args, 256, 192, 256, 16, ws, None) == E_SHAPE    # d % 128
+    assert L.mlp_relu2_fwd_fp8up(*args, 256, 128, 192, 16, ws, None) == E_SHAPE    # h % 128
+    bad = list(args)
+    bad[1] = None                                                                   # x_scale
+    assert L.mlp_relu2_fwd_fp8up(*bad, 256, 128, 256, 16, ws, None) == E_NULL
+    bad = list(args)
+    bad[7] = 0.0                                                                    # margin
+    assert L.mlp_relu2_fwd_fp8up(*bad, 256, 128, 256, 16, ws, None) == E_ARG
+    assert L.mlp_relu2_fwd_fp8up(*args, 256, 128, 256, 16, ws - 1, None) == E_WS
+    wb = L.mlp_relu2_bwd_workspace(256, 128, 256)
+    assert L.mlp_relu2_bwd_fp8post(16, 16, 16, 16, 16, None, 16, 16, 16, 0, 256, 128, 256, 16, wb,
+                                   None) == E_NULL                                  # post_scale
+    assert L.mlp_relu2_bwd_fp8post(16, 16, 16, 16, 16, 18, 16, 16, 16, 0, 256, 128, 256, 16, wb,
+                                   None) == E_ALIGN
+    assert L.mlp_relu2_bwd_fp8post(16, 16, 16, 16, 16, 16, 16, 16, 16, 2, 256, 128, 256, 16, wb,
+                                   None) == E_ARG                                   # accumulate
+    assert L.fp8_saturation_count_workspace(0) == 0 and L.fp8_saturation_count_workspace(16) > 0
+    assert L.fp8_saturation_count(16, 24, 16, 16, 1 << 20, None) == E_SHAPE          # n % 16
+    assert L.fp8_saturation_count(16, 32, None, 16, 1 << 20, None) == E_NULL
+    assert L.fp8_saturation_count(16, 32, 12, 16, 1 << 20, None) == E_ALIGN           # 8-byte count
+    assert L.fp8_saturation_count(16, 32, 16, 16, 0, None) == E_WS

@@ -190,3 +190,27 @@ def test_fp8up_full_size_sampled(fm):
     assert (O.quantize(pb, s) == pq).all()
     y = F.bf16_to_f64(bits(Y)[rows])
     assert rel_fro(y, O.down_fp8(pq, W2t, O.inv_scale(s), inv2)) < 4e-3
+
+
+def test_fp8post_full_size_sampled(fm):
+    """The e4m3-post variant at the timed workload's size: forward without
+    the bf16 post, backward from post_q; sampled rows of dX, rows of dW1 and
+    columns of dW2 against the oracle's backward on post_hat."""
+    M, d, h = synth.WORKLOADS["fwdbwd"][:3]
+    seed = synth.WORKLOADS["fwdbwd"][3]
+    ins = synth.mlp_inputs(M, d, h, seed, with_dy=True)
+    case(f"full-size fp8-post fwd+bwd M={M} d={d} h={h}")
+    blk = fm.Relu2MLP(bf16_dev(ins["W1"]), bf16_dev(ins["W2"]), margin=2.0, amax_init=1.0, keep_post=False)
+    X, dY = bf16_dev(ins["X"]), bf16_dev(ins["dY"])
+    blk.forward(X)
+    Y, post, post_q = blk.forward(X)
+    dX, dW1, dW2 = blk.backward(dY, X, None, post_q=post_q)
+    torch.cuda.synchronize()
+    assert post is None
+    rows = np.concatenate([np.arange(0, M, 1021), [255, 256, M - 1]])
+    ph = O.post_from_q(post_q.cpu().numpy(), blk.scale_used.item())
+    r1, c2 = [0, 1234, h - 1], [0, 777, h - 1]
+    bs = O.mlp_bwd_sampled(ins["dY"], ins["X"], ins["W1"], ins["W2"], ph, rows, r1, c2)
+    assert rel_fro(F.bf16_to_f64(bits(dX)[rows]), bs["dX_rows"]) < 4e-3
+    assert rel_fro(dW1.cpu().numpy()[r1].astype(np.float64), bs["dW1_rows"]) < 4e-3
+    assert rel_fro(dW2.cpu().numpy()[:, c2].astype(np.float64), bs["dW2_cols"]) < 1e-4
