@@ -114,3 +114,32 @@ def attn_inputs(M=None, d=None, qkv=None, seed=None):
         "Xo": normal_bf16((M, d), 0.5, seed, "Xo"),
         "Wo": normal_bf16((d, d), 1.0 / d, seed, "Wo"),
     }
+
+
+# Language-model head workload of the fused softcapped cross-entropy:
+# GPT-2-small shapes, the GPT-2 vocabulary padded to a multiple of 64, three
+# successive targets per position, sequences of 1024 tokens.
+CE = {"M": 49152, "d": 768, "V": 50304, "T": 3, "seq": 1024, "softcap": 15.0,
+      "weights": (1.0, 0.5, 0.25), "head_var": 4.0, "seed": 5}
+
+
+def ce_inputs(M, d, V, T, seed, seq=None, head_var=None, vocab_used=None):
+    """X [M,d] ~ N(0,1) (the final normalised hidden states), W [V,d] ~
+    N(0, head_var/d) (default 4/d: logits of standard deviation about 2), and
+    targets [M,T] int64: target j of position m is token m+1+j of a uniform
+    random token stream cut into sequences of `seq` positions (-1 past a
+    sequence's end).  `vocab_used` (default: V, or 50257 when V = 50304)
+    bounds the token ids, as a padded vocabulary leaves its tail unused."""
+    seq = M if seq is None else seq
+    hv = CE["head_var"] if head_var is None else head_var
+    if vocab_used is None:
+        vocab_used = 50257 if V == 50304 else V
+    g = rng(seed, "ce.tokens")
+    tok = g.integers(0, vocab_used, size=M + T + 1)
+    t = np.full((M, T), -1, dtype=np.int64)
+    pos = np.arange(M) % seq
+    for j in range(T):
+        ok = pos + 1 + j < seq
+        t[ok, j] = tok[np.arange(M)[ok] + 1 + j]
+    return {"X": normal_bf16((M, d), 1.0, seed, "ce.X"), "W": normal_bf16((V, d), hv / d, seed, "ce.W"),
+            "targets": t}

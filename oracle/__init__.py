@@ -14,10 +14,13 @@ Everything here is plain numpy in float64 with every rounding written out:
   fp8 W2 cache, the bf16 backward that rebuilds relu(pre) as sqrt(post),
   the weight cast-transpose, amax reduction and the FP8 linear used for the
   attention projections.
+* ``stack``    -- the layer stack around the block (RMSNorm, residual, SGD).
+* ``ce``       -- the fused softcapped cross-entropy over a language-model
+  head (loss, logit gradient, dX, dW).
 
 Parity pins: every function is checked in ``tests/test_oracle_*.py`` against
 something other than itself (the OCP e4m3 code points, torch's independent
 CPU casts, brute-force loops, closed forms, finite differences and a lossless
 special case).  Nothing in this package is "parity unpinned".
 """
-from . import formats, mlp  # noqa: F401
+from . import ce, formats, mlp, stack  # noqa: F401
