@@ -39,13 +39,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "hbm_traffic_mlp_fwd_bwd_M49152.txt")
 # GEMM kernels carry the launch site as their last template argument
 KID_NAMES = {1: "up_gemm_relu2_quant", 2: "down_gemm_e4m3", 3: "down_gemm_bf16_eval", 4: "dpost_gemm_dpre",
-             5: "dx_gemm", 6: "dw1_gemm", 7: "dw2_gemm", 8: "fp8_linear_gemm", 9: "up_gemm_e4m3_relu2_quant"}
+             5: "dx_gemm", 6: "dw1_gemm", 7: "dw2_gemm", 8: "fp8_linear_gemm", 9: "up_gemm_e4m3_relu2_quant",
+             10: "ce_head_gemm_stats", 11: "ce_head_gemm_grad", 12: "ce_dx_gemm", 13: "ce_dw_gemm"}
 OTHER_NAMES = {"k_max_final": "amax_final", "k_amax_partial": "amax_partial", "k_cast_transpose": "cast_transpose",
                "k_splitk_reduce": "splitk_reduce", "k_quantize": "quantize_e4m3", "k_fill_zero": "fill_zero",
                "k_zero_scalar": "zero_scalar", "k_scale_from_amax": "scale_from_amax", "k_amax_small": "amax_small",
                "k_transpose_weights": "transpose_weights", "k_rmsnorm_fwd": "rmsnorm_fwd", "k_rmsnorm_bwd": "rmsnorm_bwd",
                "k_add_bf16": "add_bf16", "k_sgd_bf16": "sgd_update_bf16", "k_mfma_probe": "mfma_probe",
-               "k_count_top": "count_top_codes", "k_sum_counts": "sum_counts"}
+               "k_count_top": "count_top_codes", "k_sum_counts": "sum_counts", "k_ce_rows": "ce_rows",
+               "k_ce_loss": "ce_loss"}
 
 
 def log(msg):
@@ -551,6 +553,30 @@ def extra_measurements(fm, torch, dev, X, W1, W2, dY, blk, post, post_q, Y, dX, 
         del stk
     out["margin_sweep"] = sweep
     del Xs, dYs
+
+    # fused softcapped cross-entropy over the head: M=49152, d=768, V=50304, 3 targets
+    ce = synth.CE
+    ci = synth.ce_inputs(ce["M"], ce["d"], ce["V"], ce["T"], ce["seed"], seq=ce["seq"])
+    Xc, Wc = bfd(ci["X"]), bfd(ci["W"])
+    tc = torch.from_numpy(ci["targets"].astype(np.int32)).to(dev)
+    wc = torch.tensor(ce["weights"], dtype=torch.float32, device=dev)
+    lossc = torch.zeros(1, device=dev)
+    dXc = torch.empty_like(Xc)
+    dWc = torch.empty((ce["V"], ce["d"]), dtype=torch.float32, device=dev)
+    wsc = torch.empty(fm.lib().softcap_ce_workspace(ce["M"], ce["V"], ce["d"], ce["T"]), dtype=torch.uint8,
+                      device=dev)
+    run_ce = lambda: fm.softcap_ce_fwd_bwd(Xc, Wc, tc, wc, ce["softcap"], lossc, dXc, dWc, workspace=wsc)
+    t_ce = timed(run_ce, reps=5)
+    fl_ce = 4 * 2.0 * ce["M"] * ce["d"] * ce["V"]
+    out["ce_fwd_bwd_ms"] = round(t_ce, 3)
+    out["ce_fwd_bwd_tflops"] = round(fl_ce / (t_ce * 1e-3) / 1e12, 1)
+    out["ce_frac_bf16_peak"] = round(fl_ce / (t_ce * 1e-3) / 1e12 / PEAK_BF16, 4)
+    with fm.KernelTimer(64) as kt:
+        run_ce()
+    torch.cuda.synchronize()
+    out["ce_kernels_us"] = {n: round(1e3 * t, 1) for n, t in kt.records()}
+    out["ce_loss"] = round(float(lossc.item()), 5)
+    del Xc, Wc, tc, wsc, dXc, dWc
 
     # FP8 attention projections: QKV [49152,768]x[768,2304], O [49152,768]x[768,768]
     a = synth.attn_inputs()

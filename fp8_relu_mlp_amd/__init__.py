@@ -8,8 +8,8 @@ is not built, the first call raises.
 
 Entry points (same names as the C ABI):
   mlp_relu2_fwd, mlp_relu2_fwd_fp8up, mlp_relu2_bwd, mlp_relu2_bwd_fp8post, fp8_cast_transpose, fp8_cast_transpose_w2,
-  amax_reduce, fp8_scale_from_amax, fp8_linear, fp8_saturation_count, and the
-  layer-stack helpers
+  amax_reduce, fp8_scale_from_amax, fp8_linear, fp8_saturation_count,
+  softcap_ce_fwd_bwd, and the layer-stack helpers
   rmsnorm_fwd, rmsnorm_bwd, add_bf16, sgd_update_bf16
 and ``Relu2MLP``, one MLP block's device state (bf16 weights, the transposed
 fp8 W2 cache with its scales, the delayed-scale amax carried between steps);
@@ -25,7 +25,7 @@ F32 = 0
 BF16 = 1
 
 __all__ = ["mlp_relu2_fwd", "mlp_relu2_fwd_fp8up", "mlp_relu2_bwd", "mlp_relu2_bwd_fp8post", "fp8_cast_transpose", "fp8_cast_transpose_w2", "amax_reduce",
-           "fp8_scale_from_amax", "fp8_linear", "fp8_saturation_count", "rmsnorm_fwd", "rmsnorm_bwd", "add_bf16", "sgd_update_bf16",
+           "fp8_scale_from_amax", "fp8_linear", "fp8_saturation_count", "softcap_ce_fwd_bwd", "rmsnorm_fwd", "rmsnorm_bwd", "add_bf16", "sgd_update_bf16",
            "Relu2MLP", "KernelTimer", "Fp8MlpError", "TRAIN_FP8", "EVAL_BF16"]
 
 
@@ -167,6 +167,26 @@ def fp8_saturation_count(q, count_out, workspace=None, stream=None):
     ws, wsb = _ws(L.fp8_saturation_count_workspace(n), workspace, q.device)
     check("fp8_saturation_count", L.fp8_saturation_count(_p(q) if n else None, n, _p(count_out), _p(ws), wsb,
                                                          _stream(stream)))
+
+
+def softcap_ce_fwd_bwd(X, W, targets, weights, softcap, loss_out, dX, dW, dloss=None, lse_out=None,
+                       accumulate=False, workspace=None, stream=None):
+    """Fused softcapped cross-entropy, forward and backward (see
+    include/fp8mlp.h).  X [M,d] bf16, W [V,d] bf16, targets [M,T] int32
+    (device), weights [T] fp32 (device), softcap a float (0: none),
+    loss_out [1] fp32, dX [M,d] bf16, dW [V,d] fp32.  Returns the workspace,
+    which begins with the bf16 logit gradient G [M,V]."""
+    M, d = X.shape
+    V = W.shape[0]
+    T = targets.shape[1]
+    if targets.dtype != torch.int32:
+        raise ValueError("targets must be int32")
+    L = lib()
+    ws, wsb = _ws(L.softcap_ce_workspace(M, V, d, T), workspace, X.device)
+    check("softcap_ce_fwd_bwd", L.softcap_ce_fwd_bwd(
+        _p(X), _p(W), _p(targets), T, _p(weights), float(softcap), _p(dloss), _p(loss_out), _p(lse_out), _p(dX),
+        _p(dW), int(bool(accumulate)), M, V, d, _p(ws), wsb, _stream(stream)))
+    return ws
 
 
 def rmsnorm_fwd(x, xn, inv_rms, eps=1e-6, stream=None):

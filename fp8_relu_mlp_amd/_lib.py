@@ -43,6 +43,9 @@ SIGNATURES = {
     "fp8_saturation_count": (c_int, [vp, c_i64, vp, vp, c_size, vp]),
     "fp8_linear_workspace": (c_size, [c_i64, c_i64]),
     "fp8_linear": (c_int, [vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, vp, c_size, vp]),
+    "softcap_ce_workspace": (c_size, [c_i64, c_i64, c_i64, c_int]),
+    "softcap_ce_fwd_bwd": (c_int, [vp, vp, vp, c_int, vp, c_float, vp, vp, vp, vp, vp, c_int, c_i64, c_i64, c_i64,
+                                   vp, c_size, vp]),
     "rmsnorm_fwd": (c_int, [vp, vp, vp, c_i64, c_i64, c_float, vp]),
     "rmsnorm_bwd": (c_int, [vp, vp, vp, vp, vp, c_i64, c_i64, vp]),
     "add_bf16": (c_int, [vp, vp, vp, c_i64, vp]),

@@ -38,7 +38,10 @@ enum { KC = 0, MNC = 1 };
 // Which contraction of the path a kernel instance serves.  It is a template
 // argument of the kernels only so that every launch site has its own kernel
 // symbol, which profilers report per symbol.
-enum : int { KID_UP = 1, KID_DOWN8, KID_DOWN_BF16, KID_DPOST, KID_DX, KID_DW1, KID_DW2, KID_LINEAR, KID_UP8 };
+enum : int {
+  KID_UP = 1, KID_DOWN8, KID_DOWN_BF16, KID_DPOST, KID_DX, KID_DW1, KID_DW2, KID_LINEAR, KID_UP8,
+  KID_CE_STATS, KID_CE_GRAD, KID_CE_DX, KID_CE_DW
+};
 
 template <int ELT_, int BM_, int BN_, int RB_, int STAGES_, int OCC_, int QL_, int PL_, int REG_ = 0, int NW_ = 4,
           int PELT_ = 0>

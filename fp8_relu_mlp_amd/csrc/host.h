@@ -64,6 +64,10 @@ size_t amax_ws_bytes(int64_t n);
 // most kQuantBlocks blocks (linear.hip).  When partial is given, block b
 // writes max |X| over its elements to partial[b]; *count receives the number
 // of blocks (0 for n = 0, which launches nothing).
+// out[i] = (accumulate ? out[i] : 0) + sum of the split partials part[s * n + i]
+// in split order; out[0 .. n) = 0 (n a multiple of 4; mlp_bwd.hip).
+int launch_reduce(const float* part, int splits, int64_t n, float* out, int accumulate, hipStream_t st);
+int launch_zero(float* out, int64_t n, hipStream_t st);
 constexpr int kQuantBlocks = 4096;
 constexpr size_t quantize_partial_bytes() { return (size_t)kQuantBlocks * 4; }
 int launch_quantize(const uint16_t* X, int64_t n, const float* scale, uint8_t* Xq, uint32_t* partial,

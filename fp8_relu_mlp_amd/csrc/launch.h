@@ -30,6 +30,10 @@ inline const char* kid_name(int kid) {
     case KID_DW2: return "dw2_gemm";
     case KID_LINEAR: return "fp8_linear_gemm";
     case KID_UP8: return "up_gemm_e4m3_relu2_quant";
+    case KID_CE_STATS: return "ce_head_gemm_stats";
+    case KID_CE_GRAD: return "ce_head_gemm_grad";
+    case KID_CE_DX: return "ce_dx_gemm";
+    case KID_CE_DW: return "ce_dw_gemm";
   }
   return "gemm";
 }

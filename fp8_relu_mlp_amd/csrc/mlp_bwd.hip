@@ -115,7 +115,7 @@ __global__ void __launch_bounds__(256) k_fill_zero(float4* __restrict__ out, int
     out[i] = float4{0.f, 0.f, 0.f, 0.f};
 }
 
-static int launch_reduce(const float* part, int splits, int64_t n, float* out, int accumulate, hipStream_t st) {
+int launch_reduce(const float* part, int splits, int64_t n, float* out, int accumulate, hipStream_t st) {
   const int64_t n4 = n / 4;
   int64_t blocks = cdiv(n4, 256);
   if (blocks > 4096) blocks = 4096;
@@ -125,7 +125,7 @@ static int launch_reduce(const float* part, int splits, int64_t n, float* out, i
   return launch_status();
 }
 
-static int launch_zero(float* out, int64_t n, hipStream_t st) {
+int launch_zero(float* out, int64_t n, hipStream_t st) {
   const int64_t n4 = n / 4;
   int64_t blocks = cdiv(n4, 256);
   if (blocks > 4096) blocks = 4096;

@@ -264,6 +264,36 @@ int mlp_relu2_fwd_fp8up(const uint16_t* X, const float* x_scale, const uint8_t* 
                         void* stream);
 
 /* ------------------------------------------------------------------------
+ * softcap_ce_fwd_bwd -- fused softcapped cross-entropy over a language-model
+ * head, forward and backward ("NanoGPT Speedrun (Track 1)", "From
+ * Unoptimized", "Approach" item 5: a fused softcapped cross-entropy that never
+ * materialises the [M, V] logits in fp32; "A Retrospective on Our World
+ * Records", SlowRun part: one head trained against several successive
+ * targets per position).  The pages give no formula; this computes
+ *   z = X W^T (fp32 accumulate, never stored), z' = c tanh(z / c) (z if c = 0)
+ *   lse_m = log sum_v exp(z'[m, v])
+ *   loss = (1/M) sum_m sum_j w_j (lse_m - z'[m, t[m, j]])   -> loss_out
+ *   G = bf16((dloss/M) (wsum_m softmax(z')[m, v] - sum_j w_j [v == t[m, j]])
+ *            (1 - (z'/c)^2)),   wsum_m = sum of w_j over the row's targets
+ *   dX = bf16(G W)                                          -> dX [M, d]
+ *   dW = G^T X (fp32)                                       -> dW [V, d]
+ * in two passes over the head GEMM (row statistics, then G) and two GEMMs.
+ * Arguments: X [M, d] bf16, W [V, d] bf16; targets [M, T] int32, T in 1..4
+ * (a target < 0 or >= V is no target); weights [T] fp32 (device); softcap c
+ * >= 0 (0: none); dloss: device fp32 scalar or NULL (1).  loss_out: device
+ * fp32; lse_out: device fp32 [M] or NULL.  accumulate = 1 adds into dW.
+ * V and d: multiples of 64; M >= 0 (M = 0: loss 0, dW zeroed unless
+ * accumulating).  workspace: softcap_ce_workspace(M, V, d, T) bytes; on
+ * return it begins with G ([M, V] bf16, row-major).
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_ARCH, E_ARG, E_HIP.
+ * ---------------------------------------------------------------------- */
+size_t softcap_ce_workspace(int64_t M, int64_t V, int64_t d, int T);
+int softcap_ce_fwd_bwd(const uint16_t* X, const uint16_t* W, const int32_t* targets, int T, const float* weights,
+                       float softcap, const float* dloss, float* loss_out, float* lse_out, uint16_t* dX, float* dW,
+                       int accumulate, int64_t M, int64_t V, int64_t d, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* ------------------------------------------------------------------------
  * Layer-stack helpers.  The speedrun pages train the MLP block inside a
  * pre-norm transformer and carry its FP8 state per layer from step to step
  * ("A Retrospective on Our World Records", Main Track: delayed scaling from

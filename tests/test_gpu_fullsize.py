@@ -214,3 +214,57 @@ def test_fp8post_full_size_sampled(fm):
     assert rel_fro(F.bf16_to_f64(bits(dX)[rows]), bs["dX_rows"]) < 4e-3
     assert rel_fro(dW1.cpu().numpy()[r1].astype(np.float64), bs["dW1_rows"]) < 4e-3
     assert rel_fro(dW2.cpu().numpy()[:, c2].astype(np.float64), bs["dW2_cols"]) < 1e-4
+
+
+def test_ce_full_size_sampled(fm):
+    """The fused softcapped cross-entropy at the head workload's size
+    (M=49152, d=768, V=50304, three targets, softcap 15): sampled rows of
+    lse, G and dX against the oracle, sampled columns of dW against the
+    oracle fed the GPU's G, and the loss against the oracle's reduction of
+    the GPU's lse with exact target logits."""
+    from oracle import ce as C
+    from .test_gpu_ce import U
+    cfg = synth.CE
+    M, d, V, T, c = cfg["M"], cfg["d"], cfg["V"], cfg["T"], cfg["softcap"]
+    wts = list(cfg["weights"])
+    ins = synth.ce_inputs(M, d, V, T, cfg["seed"], seq=cfg["seq"])
+    case(f"full-size softcapped CE M={M} d={d} V={V} T={T}")
+    X, W = bf16_dev(ins["X"]), bf16_dev(ins["W"])
+    t_dev = torch.from_numpy(ins["targets"].astype(np.int32)).to(DEV)
+    w_dev = torch.tensor(wts, dtype=torch.float32, device=DEV)
+    loss = torch.zeros(1, device=DEV)
+    lse = torch.zeros(M, device=DEV)
+    dX = torch.empty((M, d), dtype=torch.bfloat16, device=DEV)
+    dW = torch.empty((V, d), dtype=torch.float32, device=DEV)
+    ws = fm.softcap_ce_fwd_bwd(X, W, t_dev, w_dev, c, loss, dX, dW, lse_out=lse)
+    torch.cuda.synchronize()
+    Gd = ws[:M * V * 2].view(torch.bfloat16).view(M, V)
+    rows = np.array([0, 1, 1023, 1024, 20000, 33333, M - 1025, M - 1])
+    Xf, Wf = F.bf16_to_f64(ins["X"]), F.bf16_to_f64(ins["W"])
+    ref = C.softcap_ce(ins["X"][rows], ins["W"], ins["targets"][rows], wts, c, dloss=len(rows) / M)
+    # lse of the sampled rows, within the bound of the parity tests
+    S = np.abs(Xf[rows]) @ np.abs(Wf).T
+    ez = (d + 2) * U * S.max(axis=1) * 1.01 + 16 * U * c + 4 * U * np.abs(Xf[rows] @ Wf.T).max(axis=1)
+    e_lse = ez + (48 + 197) * U + 2.0 ** -22 + 2.0 ** -23 * np.abs(ref["lse"])
+    lse_g = lse.cpu().numpy().astype(np.float64)
+    assert (np.abs(lse_g[rows] - ref["lse"]) <= e_lse).all()
+    # loss = (1/M) sum_m sum_j w_j (lse_m - z'_t): the GPU's lse, exact target logits
+    t = ins["targets"]
+    valid = t >= 0
+    zt = np.zeros(t.shape)
+    for j in range(T):
+        m = np.nonzero(valid[:, j])[0]
+        zt[m, j] = C.softcap(np.einsum("md,md->m", Xf[m], Wf[t[m, j]]), c)
+    w = np.asarray(wts)
+    expect = (np.where(valid, w[None, :] * (lse_g[:, None] - zt), 0.0)).sum() / M
+    ez_all = (d + 2) * U * np.abs(Xf).sum(axis=1) * np.abs(Wf).max() + 16 * U * c
+    bound = (np.where(valid, w[None, :], 0.0).sum(axis=1) * ez_all).sum() / M + (512 + M / 256) * U * abs(expect)
+    assert abs(loss.item() - expect) <= bound
+    # G rows and dX rows
+    Gr = F.bf16_to_f64(bits(Gd[torch.from_numpy(rows).to(DEV)]))
+    assert rel_fro(Gr, ref["G"]) < 1e-2
+    assert rel_fro(F.bf16_to_f64(bits(dX)[rows]), Gr @ Wf) < 4e-3
+    # dW columns from the GPU's own G
+    cols = np.array([0, 7, 25000, 50256, V - 1])
+    Gc = F.bf16_to_f64(bits(Gd[:, torch.from_numpy(cols).to(DEV)].contiguous()))
+    assert rel_fro(dW.cpu().numpy()[cols].astype(np.float64), Gc.T @ Xf) < 1e-4
