@@ -77,15 +77,18 @@ def mixed_floor_us(M, d, h, fp8_gemms=1):
     return ((12 - 2 * fp8_gemms) * mdh / (PEAK_BF16 * 1e12) + 2 * fp8_gemms * mdh / (PEAK_FP8 * 1e12)) * 1e6
 
 
+# the sources the kernels of the timed step are compiled from
+STEP_SOURCES = ("abi.hip", "common.h", "epilogues.h", "gemm.h", "host.h", "launch.h", "mlp_bwd.hip", "mlp_fwd.hip")
+
+
 def kernel_source_hash():
-    """Digest of the kernel sources: HBM counters are valid only for the code they were taken on."""
+    """Digest of the step's kernel sources: HBM counters are valid only for the code they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_relu_mlp_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
+    for f in STEP_SOURCES:
+        h.update(f.encode())
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
