@@ -26,7 +26,7 @@ formula, constant or weighting; the readings are:
 """
 import numpy as np
 
-from .formats import bf16, bf16_to_f64
+from .formats import bf16, bf16_to_f64, e4m3_decode, e4m3_encode, fl32
 
 
 def exact(x):
@@ -80,3 +80,18 @@ def softcap_ce(X_bits, W_bits, targets, weights, c, dloss=1.0, rnd=bf16, Z=None)
     G = rnd(dz)
     return {"loss": float(loss), "lse": lse, "zt": zt, "G": G, "dX": rnd(G @ W), "dW": G.T @ X,
             "per_row": per_row}
+
+
+def fp8_logits(X_bits, x_scale, Wt_codes, w_inv_scale):
+    """The head's logits with both operands in e4m3 (the FP8 form of the
+    fused cross-entropy, "A Retrospective on Our World Records", SlowRun
+    part): z = (dec(e4m3(fl32(X sx))) dec(Wt)) * fl32(1/sx) * w_inv, the
+    product sums exact in float64 (every e4m3 product is a multiple of 2^-18
+    below 2^18).  Wt_codes [d, V] is the transposed e4m3 cache of W [V, d].
+    Pass the result as ``Z`` to ``softcap_ce`` (whose dX and dW stay on the
+    bf16 X and W)."""
+    X = bf16_to_f64(X_bits)
+    sx = float(np.float32(x_scale))
+    xq = e4m3_decode(e4m3_encode(fl32(X * sx)))
+    inv_sx = float(fl32(1.0 / np.float64(np.float32(sx))))
+    return (xq @ e4m3_decode(Wt_codes)) * inv_sx * float(np.float32(w_inv_scale))

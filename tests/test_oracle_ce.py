@@ -104,3 +104,34 @@ def test_loops_and_missing_targets():
     assert abs(total / 5 - out["loss"]) < 1e-12
     assert out["per_row"][4] == 0.0 and np.isnan(out["zt"][4]).all()
     assert (out["G"][4] == 0).all()
+
+
+def test_fp8_logits_lossless_and_against_torch_cast():
+    """Power-of-two scales with e4m3-exact operands: the FP8 logits equal the
+    bf16 ones exactly; random data: torch's own e4m3 cast and an exact dot
+    product over the untransposed W."""
+    from oracle import mlp as O
+    g = np.random.default_rng(44)
+    X = synth.to_bf16_bits(g.integers(-7, 8, size=(5, 16)) / 4.0)
+    Wv = g.integers(-7, 8, size=(9, 16)) / 8.0
+    Wv[0, 0] = 7 / 8
+    W = synth.to_bf16_bits(Wv)
+    Wt, s, inv, _ = O.cast_transpose(W)
+    assert s == 512.0
+    z = C.fp8_logits(X, 16.0, Wt, inv)
+    assert (z == F.bf16_to_f64(X) @ F.bf16_to_f64(W).T).all()
+    ins = synth.ce_inputs(4, 32, 64, 1, 45)
+    Wt, s, inv, _ = O.cast_transpose(ins["W"])
+    Xf = F.bf16_to_f64(ins["X"])
+    sx = O.exact_scale(O.amax(Xf))
+    z = C.fp8_logits(ins["X"], sx, Wt, inv)
+
+    def cast(v):
+        return torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+    xd, wd = cast(Xf * sx), cast(F.bf16_to_f64(ins["W"]) * s)
+    inv_sx = float(np.float32(1.0 / np.float32(sx)))
+    for m in range(4):
+        for v in range(64):
+            acc = math.fsum(xd[m, k] * wd[v, k] for k in range(32))
+            assert z[m, v] == acc * inv_sx * inv
