@@ -40,7 +40,8 @@ TRAFFIC_FILE = os.path.join(PROFILES, "hbm_traffic_mlp_fwd_bwd_M49152.txt")
 # GEMM kernels carry the launch site as their last template argument
 KID_NAMES = {1: "up_gemm_relu2_quant", 2: "down_gemm_e4m3", 3: "down_gemm_bf16_eval", 4: "dpost_gemm_dpre",
              5: "dx_gemm", 6: "dw1_gemm", 7: "dw2_gemm", 8: "fp8_linear_gemm", 9: "up_gemm_e4m3_relu2_quant",
-             10: "ce_head_gemm_stats", 11: "ce_head_gemm_grad", 12: "ce_dx_gemm", 13: "ce_dw_gemm"}
+             10: "ce_head_gemm_stats", 11: "ce_head_gemm_grad", 12: "ce_dx_gemm", 13: "ce_dw_gemm",
+             14: "ce_head_gemm_e4m3_stats", 15: "ce_head_gemm_e4m3_grad"}
 OTHER_NAMES = {"k_max_final": "amax_final", "k_amax_partial": "amax_partial", "k_cast_transpose": "cast_transpose",
                "k_splitk_reduce": "splitk_reduce", "k_quantize": "quantize_e4m3", "k_fill_zero": "fill_zero",
                "k_zero_scalar": "zero_scalar", "k_scale_from_amax": "scale_from_amax", "k_amax_small": "amax_small",
@@ -579,7 +580,28 @@ def extra_measurements(fm, torch, dev, X, W1, W2, dY, blk, post, post_q, Y, dX, 
     torch.cuda.synchronize()
     out["ce_kernels_us"] = {n: round(1e3 * t, 1) for n, t in kt.records()}
     out["ce_loss"] = round(float(lossc.item()), 5)
-    del Xc, Wc, tc, wsc, dXc, dWc
+    del wsc
+    # the FP8 head: e4m3 X (exact scale) and the transposed e4m3 W cache
+    Wtc = torch.empty((ce["d"], ce["V"]), dtype=torch.uint8, device=dev)
+    invc = torch.zeros(1, dtype=torch.float32, device=dev)
+    fm.fp8_cast_transpose(Wc, Wtc, inv_scale_out=invc)
+    amc = torch.zeros(1, dtype=torch.float32, device=dev)
+    fm.amax_reduce(Xc, amc)
+    sxc = torch.zeros(1, dtype=torch.float32, device=dev)
+    fm.fp8_scale_from_amax(amc, 1.0, sxc)
+    wsc8 = torch.empty(fm.lib().softcap_ce_fp8_workspace(ce["M"], ce["V"], ce["d"], ce["T"]), dtype=torch.uint8,
+                       device=dev)
+    run_ce8 = lambda: fm.softcap_ce_fwd_bwd_fp8(Xc, sxc, Wtc, invc, Wc, tc, wc, ce["softcap"], lossc, dXc, dWc,
+                                                workspace=wsc8)
+    t_ce8 = timed(run_ce8, reps=5)
+    out["ce_fp8_fwd_bwd_ms"] = round(t_ce8, 3)
+    out["ce_fp8_fwd_bwd_tflops"] = round(fl_ce / (t_ce8 * 1e-3) / 1e12, 1)
+    with fm.KernelTimer(64) as kt:
+        run_ce8()
+    torch.cuda.synchronize()
+    out["ce_fp8_kernels_us"] = {n: round(1e3 * t, 1) for n, t in kt.records()}
+    out["ce_fp8_loss"] = round(float(lossc.item()), 5)
+    del Xc, Wc, tc, wsc8, dXc, dWc, Wtc
 
     # FP8 attention projections: QKV [49152,768]x[768,2304], O [49152,768]x[768,768]
     a = synth.attn_inputs()

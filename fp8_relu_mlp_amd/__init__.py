@@ -9,7 +9,7 @@ is not built, the first call raises.
 Entry points (same names as the C ABI):
   mlp_relu2_fwd, mlp_relu2_fwd_fp8up, mlp_relu2_bwd, mlp_relu2_bwd_fp8post, fp8_cast_transpose, fp8_cast_transpose_w2,
   amax_reduce, fp8_scale_from_amax, fp8_linear, fp8_saturation_count,
-  softcap_ce_fwd_bwd, and the layer-stack helpers
+  softcap_ce_fwd_bwd, softcap_ce_fwd_bwd_fp8, and the layer-stack helpers
   rmsnorm_fwd, rmsnorm_bwd, add_bf16, sgd_update_bf16
 and ``Relu2MLP``, one MLP block's device state (bf16 weights, the transposed
 fp8 W2 cache with its scales, the delayed-scale amax carried between steps);
@@ -25,7 +25,8 @@ F32 = 0
 BF16 = 1
 
 __all__ = ["mlp_relu2_fwd", "mlp_relu2_fwd_fp8up", "mlp_relu2_bwd", "mlp_relu2_bwd_fp8post", "fp8_cast_transpose", "fp8_cast_transpose_w2", "amax_reduce",
-           "fp8_scale_from_amax", "fp8_linear", "fp8_saturation_count", "softcap_ce_fwd_bwd", "rmsnorm_fwd", "rmsnorm_bwd", "add_bf16", "sgd_update_bf16",
+           "fp8_scale_from_amax", "fp8_linear", "fp8_saturation_count", "softcap_ce_fwd_bwd", "softcap_ce_fwd_bwd_fp8",
+           "rmsnorm_fwd", "rmsnorm_bwd", "add_bf16", "sgd_update_bf16",
            "Relu2MLP", "KernelTimer", "Fp8MlpError", "TRAIN_FP8", "EVAL_BF16"]
 
 
@@ -186,6 +187,25 @@ def softcap_ce_fwd_bwd(X, W, targets, weights, softcap, loss_out, dX, dW, dloss=
     check("softcap_ce_fwd_bwd", L.softcap_ce_fwd_bwd(
         _p(X), _p(W), _p(targets), T, _p(weights), float(softcap), _p(dloss), _p(loss_out), _p(lse_out), _p(dX),
         _p(dW), int(bool(accumulate)), M, V, d, _p(ws), wsb, _stream(stream)))
+    return ws
+
+
+def softcap_ce_fwd_bwd_fp8(X, x_scale, Wt_q, w_inv_scale, W, targets, weights, softcap, loss_out, dX, dW,
+                           dloss=None, lse_out=None, accumulate=False, workspace=None, stream=None):
+    """The softcapped cross-entropy with the head in e4m3: Wt_q [d,V] uint8
+    (fp8_cast_transpose of W), x_scale / w_inv_scale 1-element fp32 device
+    tensors; the rest as softcap_ce_fwd_bwd.  Returns the workspace (it
+    begins with G)."""
+    M, d = X.shape
+    V = W.shape[0]
+    T = targets.shape[1]
+    if targets.dtype != torch.int32:
+        raise ValueError("targets must be int32")
+    L = lib()
+    ws, wsb = _ws(L.softcap_ce_fp8_workspace(M, V, d, T), workspace, X.device)
+    check("softcap_ce_fwd_bwd_fp8", L.softcap_ce_fwd_bwd_fp8(
+        _p(X), _p(x_scale), _p(Wt_q), _p(w_inv_scale), _p(W), _p(targets), T, _p(weights), float(softcap), _p(dloss),
+        _p(loss_out), _p(lse_out), _p(dX), _p(dW), int(bool(accumulate)), M, V, d, _p(ws), wsb, _stream(stream)))
     return ws
 
 

@@ -46,6 +46,9 @@ SIGNATURES = {
     "softcap_ce_workspace": (c_size, [c_i64, c_i64, c_i64, c_int]),
     "softcap_ce_fwd_bwd": (c_int, [vp, vp, vp, c_int, vp, c_float, vp, vp, vp, vp, vp, c_int, c_i64, c_i64, c_i64,
                                    vp, c_size, vp]),
+    "softcap_ce_fp8_workspace": (c_size, [c_i64, c_i64, c_i64, c_int]),
+    "softcap_ce_fwd_bwd_fp8": (c_int, [vp, vp, vp, vp, vp, vp, c_int, vp, c_float, vp, vp, vp, vp, vp, c_int, c_i64,
+                                       c_i64, c_i64, vp, c_size, vp]),
     "rmsnorm_fwd": (c_int, [vp, vp, vp, c_i64, c_i64, c_float, vp]),
     "rmsnorm_bwd": (c_int, [vp, vp, vp, vp, vp, c_i64, c_i64, vp]),
     "add_bf16": (c_int, [vp, vp, vp, c_i64, vp]),

@@ -11,12 +11,17 @@
 //   pass 2: the head GEMM again; G = bf16(dL/dz) in the epilogue
 //   dX = bf16(G W), dW = G^T X              (the GEMM core)
 // The logits exist only as fp32 accumulators and as the bf16 gradient G.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace fp8mlp {
 
 // X [M,d] . W [V,d]^T: both k-contiguous, two groups of four waves.
 using CfgCeHead = GemmCfg<2, 256, 256, 128, 2, 1, KC, KC, 0, 8>;
+// The FP8 form: Xq [M,d] . Wt_q [d,V] (the transposed e4m3 cache, read with
+// transposing LDS loads).
+using CfgCeHead8 = GemmCfg<1, 256, 256, 128, 2, 1, KC, MNC, 0, 8>;
 // G [M,V] . W [V,d]: G k-contiguous, W row-contiguous (k = vocabulary row).
 using CfgCeDx = GemmCfg<2, 192, 256, 128, 2, 1, KC, MNC, 0, 8>;
 // G^T . X: both row-contiguous with k = token.
@@ -40,11 +45,22 @@ struct CeParams {
   const float* weights;     // [T], device
   float c, inv_c;
   int64_t M, V;
+  const float* x_scale;     // FP8 form: z = (acc * fp32(1 / *x_scale)) * *w_inv
+  const float* w_inv;
 };
 
+// The logit of accumulator value a: the FP8 form dequantises first.
+template <bool DEQ>
+__device__ __forceinline__ float head_logit(float a, float dq_x, float dq_w) {
+  return DEQ ? (a * dq_x) * dq_w : a;
+}
+
 // Pass 1: per-row maximum and sum of exp over the tile's columns, and the
-// target logits that fall in the tile.
-struct EpiCeStats {
+// target logits that fall in the tile.  Columns follow the accumulator
+// layout of the configuration (16 consecutive per lane, or four runs of four
+// under transposed e4m3 reads).
+template <bool DEQ>
+struct EpiCeStatsT {
   CeParams p;
   float* pmax;    // [tiles_n, M]
   float* psum;    // [tiles_n, M]
@@ -55,10 +71,14 @@ struct EpiCeStats {
 
   template <class C>
   __device__ __forceinline__ void run(const TileCtx& c, f32x16 (&acc)[C::FM][C::FN], FP8MLP_LDS char* smem) {
-    static_assert(C::PERM, "needs 16 consecutive columns per lane");
     constexpr int NWN = C::NW / 2;                 // wave columns of the tile
     float* red = (float*)smem;                     // [NWN][BM][2]
     const int h = c.lane >> 5;
+    float dq_x = 1.0f, dq_w = 1.0f;
+    if constexpr (DEQ) {
+      dq_x = 1.0f / *p.x_scale;
+      dq_w = *p.w_inv;
+    }
     __syncthreads();   // every wave is done with the last pipeline stage
 #pragma unroll
     for (int fm = 0; fm < C::FM; fm++) {
@@ -67,21 +87,19 @@ struct EpiCeStats {
       float mx = -INFINITY;
 #pragma unroll
       for (int fn = 0; fn < C::FN; fn++) {
-        const int64_t n0 = c.n0 + c.wn * C::WTN + fn * 32 + 16 * h;
 #pragma unroll
         for (int e = 0; e < 16; e++) {
-          const float v = softcap_f(acc[fm][fn][e], p.c, p.inv_c);
+          const float v = softcap_f(head_logit<DEQ>(acc[fm][fn][e], dq_x, dq_w), p.c, p.inv_c);
           acc[fm][fn][e] = v;
-          if (n0 + e < p.V) mx = fmaxf(mx, v);
+          if (c.n0 + epi_col<C>(c, fn, e) < p.V) mx = fmaxf(mx, v);
         }
       }
       float s = 0.0f;
 #pragma unroll
       for (int fn = 0; fn < C::FN; fn++) {
-        const int64_t n0 = c.n0 + c.wn * C::WTN + fn * 32 + 16 * h;
 #pragma unroll
         for (int e = 0; e < 16; e++)
-          if (n0 + e < p.V) s += __expf(acc[fm][fn][e] - mx);
+          if (c.n0 + epi_col<C>(c, fn, e) < p.V) s += __expf(acc[fm][fn][e] - mx);
       }
       // the other lane half holds the same row's other 16 columns
       const float mo = __shfl_xor(mx, 32, 64), so = __shfl_xor(s, 32, 64);
@@ -95,14 +113,15 @@ struct EpiCeStats {
       if (m < p.M) {
         for (int j = 0; j < p.T; j++) {
           const int32_t t = p.targets[m * p.T + j];
+          if (t < 0 || t >= p.V) continue;
 #pragma unroll
           for (int fn = 0; fn < C::FN; fn++) {
-            const int64_t n0 = c.n0 + c.wn * C::WTN + fn * 32 + 16 * h;
-            if (t >= n0 && t < n0 + 16 && t < p.V) {
-              float v = 0.0f;
+            // the fragment's 32 columns start here; this lane holds 16 of them
+            const int64_t f0 = c.n0 + c.wn * C::WTN + fn * 32;
+            if (t >= f0 && t < f0 + 32) {
 #pragma unroll
-              for (int e = 0; e < 16; e++) v = (t - n0 == e) ? acc[fm][fn][e] : v;
-              zt[m * p.T + j] = v;
+              for (int e = 0; e < 16; e++)
+                if (c.n0 + epi_col<C>(c, fn, e) == t) zt[m * p.T + j] = acc[fm][fn][e];
             }
           }
         }
@@ -129,7 +148,8 @@ struct EpiCeStats {
 
 // Pass 2: the logit gradient, bf16, staged through LDS and stored row by row.
 //   G = bf16(g (wsum p - sum_j w_j [n == t_j]) (1 - (z'/c)^2)),  p = exp(z' - lse)
-struct EpiCeGrad {
+template <bool DEQ>
+struct EpiCeGradT {
   CeParams p;
   const float* lse;     // [M]
   const float* dloss;   // device scalar or nullptr (1)
@@ -140,10 +160,13 @@ struct EpiCeGrad {
 
   template <class C>
   __device__ __forceinline__ void run(const TileCtx& c, f32x16 (&acc)[C::FM][C::FN], FP8MLP_LDS char* smem) {
-    static_assert(C::PERM, "needs 16 consecutive columns per lane");
     using T = Tile16<C>;
     const float g = (dloss ? *dloss : 1.0f) / (float)p.M;
-    const int h = c.lane >> 5;
+    float dq_x = 1.0f, dq_w = 1.0f;
+    if constexpr (DEQ) {
+      dq_x = 1.0f / *p.x_scale;
+      dq_w = *p.w_inv;
+    }
     float w[kCeMaxTargets];
 #pragma unroll
     for (int j = 0; j < kCeMaxTargets; j++) w[j] = j < p.T ? p.weights[j] : 0.0f;
@@ -163,17 +186,17 @@ struct EpiCeGrad {
       }
 #pragma unroll
       for (int fn = 0; fn < C::FN; fn++) {
-        const int64_t n0 = c.n0 + c.wn * C::WTN + fn * 32 + 16 * h;
         uint32_t pk[8];
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
           float gv[2];
 #pragma unroll
           for (int u = 0; u < 2; u++) {
-            const float zc = softcap_f(acc[fm][fn][e + u], p.c, p.inv_c);
+            const int64_t n = c.n0 + epi_col<C>(c, fn, e + u);
+            const float zc = softcap_f(head_logit<DEQ>(acc[fm][fn][e + u], dq_x, dq_w), p.c, p.inv_c);
             float d = wsum * __expf(zc - l);
 #pragma unroll
-            for (int j = 0; j < kCeMaxTargets; j++) d -= (t[j] == n0 + e + u) ? w[j] : 0.0f;
+            for (int j = 0; j < kCeMaxTargets; j++) d -= (t[j] == n) ? w[j] : 0.0f;
             if (p.c != 0.0f) {
               const float q = zc * p.inv_c;
               d *= 1.0f - q * q;
@@ -263,39 +286,33 @@ static CePlan ce_plan(int64_t M, int64_t V, int64_t d, int T) {
   return q;
 }
 
-}  // namespace fp8mlp
-
-using namespace fp8mlp;
-
-extern "C" {
-
-size_t softcap_ce_workspace(int64_t M, int64_t V, int64_t d, int T) {
-  if (M <= 0 || V <= 0 || d <= 0 || T < 1 || T > kCeMaxTargets) return 0;
-  return ce_plan(M, V, d, T).total();
-}
-
-int softcap_ce_fwd_bwd(const uint16_t* X, const uint16_t* W, const int32_t* targets, int T, const float* weights,
-                       float softcap, const float* dloss, float* loss_out, float* lse_out, uint16_t* dX, float* dW,
-                       int accumulate, int64_t M, int64_t V, int64_t d, void* workspace, size_t workspace_bytes,
-                       void* stream) {
-  FP8MLP_REQUIRE(M >= 0 && V > 0 && d > 0 && V % 64 == 0 && d % 64 == 0 && M * V < ((int64_t)1 << 40),
+// Both entry points: FP8 selects the e4m3 head (Xq from X in the workspace,
+// Wt_q [d, V]); the gradient GEMMs run on the bf16 X and W either way.
+template <bool FP8>
+static int ce_impl(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, const float* w_inv,
+                   const uint16_t* W, const int32_t* targets, int T, const float* weights, float softcap,
+                   const float* dloss, float* loss_out, float* lse_out, uint16_t* dX, float* dW, int accumulate,
+                   int64_t M, int64_t V, int64_t d, void* workspace, size_t workspace_bytes, hipStream_t st) {
+  FP8MLP_REQUIRE(M >= 0 && V > 0 && d > 0 && V % 64 == 0 && d % (FP8 ? 128 : 64) == 0 &&
+                     M * V < ((int64_t)1 << 40),
                  FP8MLP_E_SHAPE);
   FP8MLP_REQUIRE(T >= 1 && T <= kCeMaxTargets, FP8MLP_E_ARG);
   FP8MLP_REQUIRE(softcap >= 0.0f && softcap <= 3.4e38f, FP8MLP_E_ARG);
   FP8MLP_REQUIRE(accumulate == 0 || accumulate == 1, FP8MLP_E_ARG);
   FP8MLP_REQUIRE(loss_out && dW && W && weights, FP8MLP_E_NULL);
+  if (FP8) FP8MLP_REQUIRE(x_scale && Wt_q && w_inv, FP8MLP_E_NULL);
   if (M > 0) FP8MLP_REQUIRE(X && targets && dX, FP8MLP_E_NULL);
-  for (const void* p : {(const void*)X, (const void*)W, (const void*)dX, (const void*)dW})
+  for (const void* p : {(const void*)X, (const void*)W, (const void*)Wt_q, (const void*)dX, (const void*)dW})
     FP8MLP_REQUIRE(p == nullptr || aligned16(p), FP8MLP_E_ALIGN);
   for (const void* p : {(const void*)targets, (const void*)weights, (const void*)dloss, (const void*)loss_out,
-                        (const void*)lse_out})
+                        (const void*)lse_out, (const void*)x_scale, (const void*)w_inv})
     FP8MLP_REQUIRE(((uintptr_t)p & 3) == 0, FP8MLP_E_ALIGN);
   const CePlan plan = ce_plan(M, V, d, T);
-  const size_t need = M > 0 ? plan.total() : 0;
+  const size_t xq_bytes = FP8 ? align_up((size_t)(M * d), 256) : 0;
+  const size_t need = M > 0 ? plan.total() + xq_bytes : 0;
   FP8MLP_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), FP8MLP_E_WORKSPACE);
   FP8MLP_REQUIRE(need == 0 || aligned16(workspace), FP8MLP_E_ALIGN);
   FP8MLP_TRY(check_device());
-  hipStream_t st = (hipStream_t)stream;
   if (M == 0) {
     // no positions: the loss is 0 and dW receives nothing
     {
@@ -313,13 +330,24 @@ int softcap_ce_fwd_bwd(const uint16_t* X, const uint16_t* W, const int32_t* targ
   float* lse = lse_out ? lse_out : (float*)(w + plan.g_bytes + 2 * plan.stat_bytes + plan.zt_bytes);
   float* part = (float*)(w + plan.g_bytes + 2 * plan.stat_bytes + plan.zt_bytes + plan.lse_bytes);
   float* dw_part = (float*)((char*)part + plan.part_bytes);
-  CeParams p{targets, T, weights, softcap, softcap > 0.0f ? 1.0f / softcap : 0.0f, M, V};
+  CeParams p{targets, T, weights, softcap, softcap > 0.0f ? 1.0f / softcap : 0.0f, M, V, x_scale, w_inv};
 
-  const GemmArgs head{X, d, W, d, M, V, d, (int)plan.tiles_m, (int)plan.tiles_n, 1, d};
+  // the head: X W^T in bf16, or e4m3(X * x_scale) . Wt_q
+  using CH = typename std::conditional<FP8, CfgCeHead8, CfgCeHead>::type;
+  static_assert(CH::BM == CfgCeHead::BM && CH::BN == CfgCeHead::BN, "one tiling of the statistics");
+  GemmArgs head{X, d, W, d, M, V, d, (int)plan.tiles_m, (int)plan.tiles_n, 1, d};
+  if constexpr (FP8) {
+    uint8_t* Xq = (uint8_t*)w + plan.total();
+    int64_t nx = 0;
+    FP8MLP_TRY(launch_quantize(X, M * d, x_scale, Xq, nullptr, &nx, st));
+    head.q = Xq;
+    head.p = Wt_q;
+    head.ldp = V;
+  }
   // pass 1: row statistics and target logits
   {
-    EpiCeStats epi{p, pmax, psum, zt};
-    FP8MLP_TRY(launch_gemm<CfgCeHead, KID_CE_STATS>(head, epi, st));
+    EpiCeStatsT<FP8> epi{p, pmax, psum, zt};
+    FP8MLP_TRY((launch_gemm<CH, FP8 ? KID_CE8_STATS : KID_CE_STATS>(head, epi, st)));
   }
   {
     TraceScope trace("ce_rows", st);
@@ -334,8 +362,8 @@ int softcap_ce_fwd_bwd(const uint16_t* X, const uint16_t* W, const int32_t* targ
   }
   // pass 2: the logit gradient
   {
-    EpiCeGrad epi{p, lse, dloss, G};
-    FP8MLP_TRY(launch_gemm<CfgCeHead, KID_CE_GRAD>(head, epi, st));
+    EpiCeGradT<FP8> epi{p, lse, dloss, G};
+    FP8MLP_TRY((launch_gemm<CH, FP8 ? KID_CE8_GRAD : KID_CE_GRAD>(head, epi, st)));
   }
   // dX = G W
   {
@@ -353,6 +381,39 @@ int softcap_ce_fwd_bwd(const uint16_t* X, const uint16_t* W, const int32_t* targ
   EpiF32 epi{dw_part, d, V * d, 0};
   FP8MLP_TRY(launch_gemm<CfgCeDw, KID_CE_DW>(a, epi, st));
   return launch_reduce(dw_part, plan.dw_splits, V * d, dW, accumulate, st);
+}
+
+}  // namespace fp8mlp
+
+using namespace fp8mlp;
+
+extern "C" {
+
+size_t softcap_ce_workspace(int64_t M, int64_t V, int64_t d, int T) {
+  if (M <= 0 || V <= 0 || d <= 0 || T < 1 || T > kCeMaxTargets) return 0;
+  return ce_plan(M, V, d, T).total();
+}
+
+size_t softcap_ce_fp8_workspace(int64_t M, int64_t V, int64_t d, int T) {
+  if (M <= 0 || V <= 0 || d <= 0 || T < 1 || T > kCeMaxTargets) return 0;
+  return ce_plan(M, V, d, T).total() + align_up((size_t)(M * d), 256);
+}
+
+int softcap_ce_fwd_bwd(const uint16_t* X, const uint16_t* W, const int32_t* targets, int T, const float* weights,
+                       float softcap, const float* dloss, float* loss_out, float* lse_out, uint16_t* dX, float* dW,
+                       int accumulate, int64_t M, int64_t V, int64_t d, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return ce_impl<false>(X, nullptr, nullptr, nullptr, W, targets, T, weights, softcap, dloss, loss_out, lse_out, dX,
+                        dW, accumulate, M, V, d, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int softcap_ce_fwd_bwd_fp8(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, const float* w_inv_scale,
+                           const uint16_t* W, const int32_t* targets, int T, const float* weights, float softcap,
+                           const float* dloss, float* loss_out, float* lse_out, uint16_t* dX, float* dW,
+                           int accumulate, int64_t M, int64_t V, int64_t d, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return ce_impl<true>(X, x_scale, Wt_q, w_inv_scale, W, targets, T, weights, softcap, dloss, loss_out, lse_out, dX,
+                       dW, accumulate, M, V, d, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 }  // extern "C"

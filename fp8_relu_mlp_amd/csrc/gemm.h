@@ -40,7 +40,7 @@ enum { KC = 0, MNC = 1 };
 // symbol, which profilers report per symbol.
 enum : int {
   KID_UP = 1, KID_DOWN8, KID_DOWN_BF16, KID_DPOST, KID_DX, KID_DW1, KID_DW2, KID_LINEAR, KID_UP8,
-  KID_CE_STATS, KID_CE_GRAD, KID_CE_DX, KID_CE_DW
+  KID_CE_STATS, KID_CE_GRAD, KID_CE_DX, KID_CE_DW, KID_CE8_STATS, KID_CE8_GRAD
 };
 
 template <int ELT_, int BM_, int BN_, int RB_, int STAGES_, int OCC_, int QL_, int PL_, int REG_ = 0, int NW_ = 4,

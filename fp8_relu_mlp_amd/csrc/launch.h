@@ -34,6 +34,8 @@ inline const char* kid_name(int kid) {
     case KID_CE_GRAD: return "ce_head_gemm_grad";
     case KID_CE_DX: return "ce_dx_gemm";
     case KID_CE_DW: return "ce_dw_gemm";
+    case KID_CE8_STATS: return "ce_head_gemm_e4m3_stats";
+    case KID_CE8_GRAD: return "ce_head_gemm_e4m3_grad";
   }
   return "gemm";
 }

@@ -294,6 +294,25 @@ int softcap_ce_fwd_bwd(const uint16_t* X, const uint16_t* W, const int32_t* targ
                        void* stream);
 
 /* ------------------------------------------------------------------------
+ * softcap_ce_fwd_bwd_fp8 -- the same loss and gradients with the head in e4m3
+ * ("A Retrospective on Our World Records", SlowRun part: the fused FP8
+ * soft-capped cross-entropy):
+ *   z = (e4m3(fp32(X * *x_scale)) . Wt_q) * fp32(1 / *x_scale) * *w_inv_scale
+ * (fp32 accumulate), then everything as in softcap_ce_fwd_bwd; dX = bf16(G W)
+ * and dW = G^T X use the bf16 X and W.  Wt_q [d, V] e4m3 is the transposed
+ * cache of W (fp8_cast_transpose of W [V, d]) with its dequantisation
+ * multiplier w_inv_scale; x_scale: device fp32.  d: a multiple of 128.
+ * workspace: softcap_ce_fp8_workspace(M, V, d, T) bytes (it begins with G).
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_ARCH, E_ARG, E_HIP.
+ * ---------------------------------------------------------------------- */
+size_t softcap_ce_fp8_workspace(int64_t M, int64_t V, int64_t d, int T);
+int softcap_ce_fwd_bwd_fp8(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, const float* w_inv_scale,
+                           const uint16_t* W, const int32_t* targets, int T, const float* weights, float softcap,
+                           const float* dloss, float* loss_out, float* lse_out, uint16_t* dX, float* dW,
+                           int accumulate, int64_t M, int64_t V, int64_t d, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
  * Layer-stack helpers.  The speedrun pages train the MLP block inside a
  * pre-norm transformer and carry its FP8 state per layer from step to step
  * ("A Retrospective on Our World Records", Main Track: delayed scaling from

@@ -12,7 +12,11 @@ Gates (element by element on the same seeded inputs):
     oracle's (the bf16-path gate);
   * dX within 4e-3 and dW within 1e-4 of the oracle fed the GPU's own G (one
     bf16 rounding of dX; fp32 accumulation only for dW);
-  * no-softcap, missing and out-of-range targets, accumulation, M = 0.
+  * no-softcap, missing and out-of-range targets, accumulation, M = 0;
+  * the FP8 head (softcap_ce_fwd_bwd_fp8): the transposed e4m3 W cache
+    bit-exact, the logits' error bounded by the e4m3 matrix core's alignment
+    window (``acc_bound`` of the FP8 up-projection tests) and the two fp32
+    dequantisation products, the rest as above.
 """
 import numpy as np
 import pytest
@@ -130,3 +134,63 @@ def test_ce_empty(fm):
     ins = synth.ce_inputs(0, 128, 256, 2, 85)
     g = run(fm, ins, [1.0, 0.5], 15.0)
     assert g["loss"] == 0.0 and (g["dW"] == 0).all()
+
+
+# ------------------------------------------------------------------ FP8 head
+def run_fp8(fm, ins, weights, c):
+    from oracle import mlp as O
+    X, W = bf16_dev(ins["X"]), bf16_dev(ins["W"])
+    M, d = ins["X"].shape
+    V = ins["W"].shape[0]
+    Wt = torch.empty((d, V), dtype=torch.uint8, device=DEV)
+    inv = torch.zeros(1, dtype=torch.float32, device=DEV)
+    fm.fp8_cast_transpose(W, Wt, inv_scale_out=inv)
+    sx = O.exact_scale(O.amax(F.bf16_to_f64(ins["X"])))
+    t = torch.from_numpy(ins["targets"].astype(np.int32)).to(DEV)
+    w = torch.tensor(weights, dtype=torch.float32, device=DEV)
+    loss, lse = torch.zeros(1, device=DEV), torch.zeros(M, device=DEV)
+    dX = torch.empty((M, d), dtype=torch.bfloat16, device=DEV)
+    dW = torch.empty((V, d), dtype=torch.float32, device=DEV)
+    ws = fm.softcap_ce_fwd_bwd_fp8(X, torch.tensor([sx], dtype=torch.float32, device=DEV), Wt, inv, W, t, w, c,
+                                   loss, dX, dW, lse_out=lse)
+    torch.cuda.synchronize()
+    return {"loss": float(loss.item()), "lse": lse.cpu().numpy().astype(np.float64),
+            "G": bits(ws[:M * V * 2].view(torch.bfloat16).view(M, V)), "dX": F.bf16_to_f64(bits(dX)),
+            "dW": dW.cpu().numpy().astype(np.float64), "Wt": Wt.cpu().numpy(), "inv": float(inv.item()), "sx": sx}
+
+
+def check_fp8(ins, g, weights, c):
+    from oracle import mlp as O
+    from .test_gpu_fp8up import acc_bound
+    Wt, _, inv, _ = O.cast_transpose(ins["W"])
+    assert (Wt == g["Wt"]).all() and inv == g["inv"]
+    Z = C.fp8_logits(ins["X"], g["sx"], Wt, inv)
+    ref = C.softcap_ce(ins["X"], ins["W"], ins["targets"], weights, c if c else float("inf"), Z=Z)
+    X = F.bf16_to_f64(ins["X"])
+    xq = F.e4m3_decode(F.e4m3_encode(F.fl32(X * g["sx"])))
+    a = O.inv_scale(g["sx"]) * inv
+    ez = ((acc_bound(xq, F.e4m3_decode(Wt)) * a).max(axis=1) * 1.001 + 4 * U * np.abs(Z).max(axis=1)
+          + 16 * U * (c if c else 0.0))
+    V = ins["W"].shape[0]
+    tiles = -(-V // 256)
+    e_lse = ez + (48 + tiles) * U + 2.0 ** -22 + 2.0 ** -23 * np.abs(ref["lse"])
+    assert (np.abs(g["lse"] - ref["lse"]) <= e_lse).all()
+    t = ins["targets"]
+    valid = (t >= 0) & (t < V)
+    M = t.shape[0]
+    wsum = np.where(valid, np.asarray(weights)[None, :], 0.0).sum(axis=1)
+    eloss = (wsum * (e_lse + ez)).sum() / M + (256 + M / 256 + 8) * U * np.abs(ref["per_row"]).sum() / M
+    assert abs(g["loss"] - ref["loss"]) <= eloss, (g["loss"], ref["loss"], eloss)
+    Gg = F.bf16_to_f64(g["G"])
+    assert rel_fro(Gg, ref["G"]) < 1e-2
+    assert rel_fro(g["dX"], Gg @ F.bf16_to_f64(ins["W"])) < 4e-3
+    assert rel_fro(g["dW"], Gg.T @ X) < 1e-4
+
+
+@pytest.mark.parametrize("M,d,V,T,c", [(300, 128, 1024, 3, 15.0), (257, 256, 832, 2, 5.0), (777, 768, 4096, 3, 30.0),
+                                       (64, 128, 256, 1, 0.0)])
+def test_ce_fp8_head(fm, M, d, V, T, c):
+    case(f"ce fp8 head M={M} d={d} V={V} T={T} c={c}")
+    ins = synth.ce_inputs(M, d, V, T, 90 + M, seq=100, head_var=16.0)
+    w = [1.0, 0.5, 0.25][:T]
+    check_fp8(ins, run_fp8(fm, ins, w, c), w, c)
