@@ -268,3 +268,54 @@ def test_ce_full_size_sampled(fm):
     cols = np.array([0, 7, 25000, 50256, V - 1])
     Gc = F.bf16_to_f64(bits(Gd[:, torch.from_numpy(cols).to(DEV)].contiguous()))
     assert rel_fro(dW.cpu().numpy()[cols].astype(np.float64), Gc.T @ Xf) < 1e-4
+
+
+def test_ce_fp8_full_size_sampled(fm):
+    """The FP8-head cross-entropy at the head workload's size: the e4m3 W
+    cache bit-exact, sampled rows of lse and G against the oracle on the
+    e4m3 logits (lse within the alignment-window bound), dX rows and dW
+    columns against the oracle fed the GPU's G."""
+    from oracle import ce as C
+    from .test_gpu_ce import U
+    from .test_gpu_fp8up import acc_bound
+    cfg = synth.CE
+    M, d, V, T, c = cfg["M"], cfg["d"], cfg["V"], cfg["T"], cfg["softcap"]
+    wts = list(cfg["weights"])
+    ins = synth.ce_inputs(M, d, V, T, cfg["seed"], seq=cfg["seq"])
+    case(f"full-size FP8-head softcapped CE M={M} d={d} V={V} T={T}")
+    X, W = bf16_dev(ins["X"]), bf16_dev(ins["W"])
+    Wt = torch.empty((d, V), dtype=torch.uint8, device=DEV)
+    inv = torch.zeros(1, dtype=torch.float32, device=DEV)
+    fm.fp8_cast_transpose(W, Wt, inv_scale_out=inv)
+    am = torch.zeros(1, dtype=torch.float32, device=DEV)
+    fm.amax_reduce(X, am)
+    sx = torch.zeros(1, dtype=torch.float32, device=DEV)
+    fm.fp8_scale_from_amax(am, 1.0, sx)
+    t_dev = torch.from_numpy(ins["targets"].astype(np.int32)).to(DEV)
+    w_dev = torch.tensor(wts, dtype=torch.float32, device=DEV)
+    loss, lse = torch.zeros(1, device=DEV), torch.zeros(M, device=DEV)
+    dX = torch.empty((M, d), dtype=torch.bfloat16, device=DEV)
+    dW = torch.empty((V, d), dtype=torch.float32, device=DEV)
+    ws = fm.softcap_ce_fwd_bwd_fp8(X, sx, Wt, inv, W, t_dev, w_dev, c, loss, dX, dW, lse_out=lse)
+    torch.cuda.synchronize()
+    Wt_o, _, inv_o, _ = O.cast_transpose(ins["W"])
+    assert (Wt.cpu().numpy() == Wt_o).all() and inv.item() == inv_o
+    sxv = float(sx.item())
+    assert f32_bits(sxv) == f32_bits(O.exact_scale(O.amax(F.bf16_to_f64(ins["X"]))))
+    rows = np.array([0, 1023, 1024, 30000, M - 1])
+    Z = C.fp8_logits(ins["X"][rows], sxv, Wt_o, inv_o)
+    ref = C.softcap_ce(ins["X"][rows], ins["W"], ins["targets"][rows], wts, c, dloss=len(rows) / M, Z=Z)
+    Xf, Wf = F.bf16_to_f64(ins["X"]), F.bf16_to_f64(ins["W"])
+    xq = F.e4m3_decode(F.e4m3_encode(F.fl32(Xf[rows] * sxv)))
+    ez = ((acc_bound(xq, F.e4m3_decode(Wt_o)) * O.inv_scale(sxv) * inv_o).max(axis=1) * 1.001
+          + 4 * U * np.abs(Z).max(axis=1) + 16 * U * c)
+    e_lse = ez + (48 + 197) * U + 2.0 ** -22 + 2.0 ** -23 * np.abs(ref["lse"])
+    lse_g = lse.cpu().numpy().astype(np.float64)
+    assert (np.abs(lse_g[rows] - ref["lse"]) <= e_lse).all()
+    Gd = ws[:M * V * 2].view(torch.bfloat16).view(M, V)
+    Gr = F.bf16_to_f64(bits(Gd[torch.from_numpy(rows).to(DEV)]))
+    assert rel_fro(Gr, ref["G"]) < 1e-2
+    assert rel_fro(F.bf16_to_f64(bits(dX)[rows]), Gr @ Wf) < 4e-3
+    cols = np.array([3, 25001, V - 1])
+    Gc = F.bf16_to_f64(bits(Gd[:, torch.from_numpy(cols).to(DEV)].contiguous()))
+    assert rel_fro(dW.cpu().numpy()[cols].astype(np.float64), Gc.T @ Xf) < 1e-4
