@@ -161,3 +161,17 @@ def test_variant_entry_points_validation(L):
     assert L.fp8_saturation_count(16, 32, None, 16, 1 << 20, None) == E_NULL
     assert L.fp8_saturation_count(16, 32, 12, 16, 1 << 20, None) == E_ALIGN           # 8-byte count
     assert L.fp8_saturation_count(16, 32, 16, 16, 0, None) == E_WS
+
+
+def test_product_path_fails_loudly(monkeypatch):
+    """No CPU fallback: without the built library the first call raises, and
+    tensors outside GPU memory are refused before any call."""
+    import torch
+    import fp8_relu_mlp_amd as fm
+    from fp8_relu_mlp_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libfp8mlp.so")
+    with pytest.raises(ImportError):
+        fm.amax_reduce(torch.zeros(16), torch.zeros(1))
+    with pytest.raises(ValueError):
+        fm._p(torch.zeros(4))
