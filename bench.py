@@ -183,6 +183,32 @@ def summarize_profiles(outdir):
         fh.write("\n")
     print(f"wrote {PROFILES}/kernel_trace_mlp_fwd_bwd_M49152.md, hbm_traffic_mlp_fwd_bwd_M49152.md, {TRAFFIC_FILE}")
 
+    # matrix-core counters (optional run): executed MFMA work and busy share
+    if os.path.isdir(os.path.join(outdir, "mfma")):
+        acc = {}
+        for r in rows("mfma", "*counter_collection.csv"):
+            n = logical_kernel_name(r["Kernel_Name"])
+            acc.setdefault(n, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        avg = {n: {c: sum(v) / len(v) for c, v in cs.items()} for n, cs in acc.items()}
+        cmd = ("rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8 "
+               f"SQ_INSTS_VALU_MFMA_MOPS_F6F4 --output-format csv -d OUT/mfma -o m -- {cmd_bench}")
+        lines = ["# Matrix-core counters per launch: fused FP8 ReLU^2 MLP fwd+bwd, M=49152 d=768 h=3072 (one MI355X)",
+                 "", "Command (from a scratch directory, TMPDIR=/tmp):", "", f"    {cmd}", "",
+                 "MFMA GFLOP = (SQ_INSTS_VALU_MFMA_MOPS_BF16 + _F8 + _F6F4) x 512 (the counters count multiply-",
+                 "adds / 512); `MfmaUtil` = busy cycles of the matrix cores over all SIMDs / (GPU active cycles x",
+                 "SIMDs), in per cent, so it folds in the clock the kernel actually ran at.", "",
+                 "| kernel | MFMA GFLOP | algorithmic GFLOP | MfmaUtil % |", "|---|---:|---:|---:|"]
+        for n in sorted(avg, key=lambda k: -avg[k].get("MfmaUtil", 0.0)):
+            c = avg[n]
+            gf = 512.0 * sum(c.get(x, 0.0) for x in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8",
+                                                      "SQ_INSTS_VALU_MFMA_MOPS_F6F4")) / 1e9
+            alg = f"{work[n][0] / 1e9:.1f}" if n in work else ""
+            lines.append(f"| {n} | {gf:.1f} | {alg} | {c.get('MfmaUtil', float('nan')):.1f} |")
+        lines += ["", f"Kernel sources digest: `{kernel_source_hash()}`"]
+        with open(os.path.join(PROFILES, "mfma_counters_mlp_fwd_bwd_M49152.md"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        print(f"wrote {PROFILES}/mfma_counters_mlp_fwd_bwd_M49152.md")
+
 
 def measured_traffic():
     """Per-launch HBM bytes from the committed counter summary, or {} when
@@ -423,6 +449,52 @@ def extra_measurements(fm, torch, dev, X, W1, W2, dY, blk, post, post_q, Y, dX, 
                                                   workspace=ws_c))
     out["w2_refresh_us"] = round(t_w2 * 1e3, 2)
     out["w2_refresh_gbs_alg"] = round((D * H * 2 * 2 + D * H) / (t_w2 * 1e-3) / 1e9, 1)
+
+    # the naive unfused forward the pages warn about: the up-projection stores
+    # only post, a separate pass rescans it for amax, another quantises it,
+    # then the FP8 down-projection (fp8_linear = quantise pass + e4m3 GEMM);
+    # summed kernel durations, against the fused forward's
+    amx, sxn = torch.zeros(1, dtype=torch.float32, device=dev), torch.zeros(1, dtype=torch.float32, device=dev)
+    ws_a = torch.empty(max(1, fm.lib().amax_reduce_workspace(M * H)), dtype=torch.uint8, device=dev)
+    ws_l = torch.empty(max(1, fm.lib().fp8_linear_workspace(M, H)), dtype=torch.uint8, device=dev)
+
+    def naive():
+        blk.forward(X, mode=fm.EVAL_BF16, post=post, Y=Y, carry=False, workspace=ws_f)
+        fm.amax_reduce(post, amx, workspace=ws_a)
+        fm.fp8_scale_from_amax(amx, MARGIN, sxn)
+        fm.fp8_linear(post, sxn, blk.W2t_q, blk.w2_inv_scale, Y, workspace=ws_l)
+
+    def kernel_sums(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        with fm.KernelTimer(256 * reps) as kt:
+            for _ in range(reps):
+                fn()
+        torch.cuda.synchronize()
+        acc = {}
+        for name, t in kt.records():
+            acc[name] = acc.get(name, 0.0) + 1e3 * t / reps
+        return acc
+
+    kn = kernel_sums(naive)
+    kf = kernel_sums(lambda: blk.forward(X, post=post, post_q=post_q, Y=Y, carry=False, workspace=ws_f))
+    naive_parts = {k: round(v, 1) for k, v in kn.items() if k != "down_gemm_bf16_eval"}
+    out["naive_unfused_fwd_us"] = round(sum(naive_parts.values()), 1)
+    out["naive_unfused_fwd_parts_us"] = naive_parts
+    out["fused_fwd_kernels_us"] = round(sum(kf.values()), 1)
+    del ws_l
+
+    # cast-transpose and amax at large sizes (HBM-bound): [49152, 3072] bf16
+    Wbig = post.view(M, H)
+    Wt_big = torch.empty((H, M), dtype=torch.uint8, device=dev)
+    ws_big = torch.empty(max(1, fm.lib().fp8_cast_transpose_workspace(M, H)), dtype=torch.uint8, device=dev)
+    t_cb = timed(lambda: fm.fp8_cast_transpose(Wbig, Wt_big, scale_in=sxn, workspace=ws_big))
+    out["cast_transpose_49152x3072_us"] = round(t_cb * 1e3, 1)
+    out["cast_transpose_49152x3072_gbs"] = round((M * H * 3) / (t_cb * 1e-3) / 1e9, 1)
+    t_ab = timed(lambda: fm.amax_reduce(post, amx, workspace=ws_a))
+    out["amax_reduce_post_us"] = round(t_ab * 1e3, 1)
+    out["amax_reduce_post_gbs"] = round((M * H * 2) / (t_ab * 1e-3) / 1e9, 1)
+    del Wt_big, ws_big, ws_a
 
     # the same step with both forward GEMMs in e4m3
     blk8 = fm.Relu2MLP(W1, W2, margin=MARGIN, amax_init=1.0, fp8_up=True)
