@@ -266,8 +266,8 @@ def main():
         summarize_profiles(args.summarize_profiles)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); multi-GPU runs are not part of "
-              "this build: the data-parallel sharding is described in DESIGN.md", file=sys.stderr)
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the multi-GPU data-parallel path is "
+              "not implemented, so there is no figure for more than one GPU", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
