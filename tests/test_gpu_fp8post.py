@@ -165,3 +165,31 @@ def test_fp8post_block_and_stack(fm):
         assert np.isfinite(st).all()
         assert all(torch.isfinite(blk_.W1.float()).all() and torch.isfinite(blk_.W2.float()).all()
                    for blk_ in stk.layers)
+
+
+def test_fp8up_without_bf16_post(fm):
+    """Both variants at once (M=4096, d=768, h=3072): the e4m3 up-projection
+    writing only post_q gives the same codes, amax and Y as with post kept,
+    and the backward on those codes matches the oracle on post_hat."""
+    M, d, h = 4096, 768, 3072
+    ins = synth.mlp_inputs(M, d, h, 76, with_dy=True)
+    case("fp8up + fp8post, block pair")
+    W1, W2 = bf16_dev(ins["W1"]), bf16_dev(ins["W2"])
+    X, dY = bf16_dev(ins["X"]), bf16_dev(ins["dY"])
+    keep = fm.Relu2MLP(W1, W2, amax_init=1.0, fp8_up=True)
+    drop = fm.Relu2MLP(W1, W2, amax_init=1.0, fp8_up=True, keep_post=False)
+    for blk in (keep, drop):
+        blk.forward(X)                                   # bootstrap both amaxes
+    Yk, post_k, q_k = keep.forward(X)
+    Yd, post_d, q_d = drop.forward(X)
+    dX, dW1, dW2 = drop.backward(dY, X, None, post_q=q_d)
+    torch.cuda.synchronize()
+    assert post_d is None
+    assert (q_k.cpu().numpy() == q_d.cpu().numpy()).all()
+    assert (bits(Yk) == bits(Yd)).all()
+    assert f32_bits(keep.amax_last.item()) == f32_bits(drop.amax_last.item())
+    ph = O.post_from_q(q_d.cpu().numpy(), drop.scale_used.item())
+    ref = O.mlp_bwd(ins["dY"], ins["X"], ins["W1"], ins["W2"], ph)
+    assert rel_fro(F.bf16_to_f64(bits(dX)), ref["dX"]) < 4e-3
+    assert rel_fro(dW1.cpu().numpy().astype(np.float64), ref["dW1"]) < 4e-3
+    assert rel_fro(dW2.cpu().numpy().astype(np.float64), ref["dW2"]) < 1e-4
