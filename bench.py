@@ -610,6 +610,11 @@ def extra_measurements(fm, torch, dev, X, W1, W2, dY, blk, post, post_q, Y, dX, 
     t_stack8 = stack_run(fp8_up=True)
     out["stack_12x8_fp8up_ms"] = round(t_stack8, 2)
     out["stack_12x8_fp8up_tflops"] = round(fl_stack / (t_stack8 * 1e-3) / 1e12, 1)
+    t_stackq = stack_run(keep_post=False)
+    out["stack_12x8_fp8post_ms"] = round(t_stackq, 2)
+    t_stackb = stack_run(fp8_up=True, keep_post=False)
+    out["stack_12x8_fp8up_fp8post_ms"] = round(t_stackb, 2)
+    out["stack_12x8_fp8up_fp8post_tflops"] = round(fl_stack / (t_stackb * 1e-3) / 1e12, 1)
 
     # margin / window sweep with the top-code telemetry (share of e4m3 post
     # codes at 448 per layer and step, bootstrap step excluded)
