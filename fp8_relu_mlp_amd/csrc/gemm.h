@@ -44,7 +44,7 @@ enum : int {
 };
 
 template <int ELT_, int BM_, int BN_, int RB_, int STAGES_, int OCC_, int QL_, int PL_, int REG_ = 0, int NW_ = 4,
-          int PELT_ = 0>
+          int PELT_ = 0, int QB_ = 2>
 struct GemmCfg {
   static constexpr int ELT = ELT_;                 // bytes per element: 2 bf16, 1 e4m3
   // bytes per element of the P operand in memory and LDS (default ELT).
@@ -75,7 +75,11 @@ struct GemmCfg {
   static constexpr int SL = RB / KSTEP;            // MFMA k-steps per tile
   static constexpr int Q_BYTES = BM * RB, P_BYTES = BN * BK * PELT;
   static constexpr int STAGE_BYTES = Q_BYTES + P_BYTES;
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  // QB == 3 (two-group kernel only): three Q buffers beside the two P
+  // buffers, so each Q k-tile is loaded two k-tiles ahead of its use and only
+  // the P share has to arrive within one.
+  static constexpr int QB = QB_;
+  static constexpr int LDS_BYTES = QB == 3 ? 3 * Q_BYTES + 2 * P_BYTES : STAGES * STAGE_BYTES;
   static constexpr int Q_LOADS = Q_BYTES / (1024 * NW);   // 16 B x 64 lanes x NW waves per round
   static constexpr int P_LOADS = P_BYTES / (1024 * NW);
   static constexpr int LOADS = Q_LOADS + P_LOADS;
@@ -90,6 +94,7 @@ struct GemmCfg {
   static_assert(WTN % 32 == 0 && WTM % 32 == 0, "wave tile");
   static_assert(Q_BYTES % (1024 * NW) == 0 && P_BYTES % (1024 * NW) == 0, "loads");
   static_assert(NW == 4 || (REG == 0 && STAGES == 2 && OCC == 1), "the two-group kernel: direct loads, two buffers");
+  static_assert(QB == 2 || (QB == 3 && NW == 8), "three Q buffers: the two-group kernel");
   // the row-contiguous swizzle XORs bits 6-7 (bf16) or 4-6 (e4m3) of the byte offset
   static_assert(QL == KC || (BM * ELT) % (ELT == 2 ? 256 : 128) == 0, "row-contiguous Q tile rows");
   static_assert(PL == KC || (BN * PELT) % (PELT == 2 ? 256 : 128) == 0, "row-contiguous P tile rows");
@@ -356,6 +361,17 @@ struct TileLoads {
     const uint32_t dq = (uint32_t)kt * qstep, dp = (uint32_t)kt * pstep;
 #pragma unroll
     for (int j = 0; j < C::Q_LOADS; j++) buffer_load_lds16(rq, sq + (j * C::NW + wave) * 1024, qoff[j] + dq);
+#pragma unroll
+    for (int j = 0; j < C::P_LOADS; j++) buffer_load_lds16(rp, sp + (j * C::NW + wave) * 1024, poff[j] + dp);
+  }
+  // only the Q (or only the P) share of k-tile kt, to LDS address sq (sp)
+  __device__ __forceinline__ void issue_q(FP8MLP_LDS char* sq, int kt, int wave) const {
+    const uint32_t dq = (uint32_t)kt * qstep;
+#pragma unroll
+    for (int j = 0; j < C::Q_LOADS; j++) buffer_load_lds16(rq, sq + (j * C::NW + wave) * 1024, qoff[j] + dq);
+  }
+  __device__ __forceinline__ void issue_p(FP8MLP_LDS char* sp, int kt, int wave) const {
+    const uint32_t dp = (uint32_t)kt * pstep;
 #pragma unroll
     for (int j = 0; j < C::P_LOADS; j++) buffer_load_lds16(rp, sp + (j * C::NW + wave) * 1024, poff[j] + dp);
   }
@@ -668,6 +684,7 @@ template <class C, class Epi, int KID>
 __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs a, Epi epi) {
   static_assert(C::NW == 8 && C::STAGES == 2 && C::REG == 0 && C::OCC == 1, "two-group kernel");
   static_assert(C::SL % 2 == 0, "k-slices split into two phases");
+  constexpr bool Q3 = C::QB == 3;
   constexpr int EPI_BYTES = Epi::template lds_bytes<C>();
   constexpr int SMEM = C::LDS_BYTES > EPI_BYTES ? C::LDS_BYTES : EPI_BYTES;
   static_assert(SMEM <= 160 * 1024, "LDS with the epilogue's staging");
@@ -677,7 +694,6 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs a, Epi epi) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = wave >> 2, wm = (wave >> 1) & 1, wn = 2 * (wave & 1) + g;
   side_amax(a, wave, lane);
-
   const TilePos t = tile_pos<C>(a);
   const int KT = t.KT;
   TileLoads<C> ld;
@@ -686,6 +702,13 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs a, Epi epi) {
   fr.init(wm, wn, lane);
   using Frag = typename FragT<C::ELT>::type;
   constexpr int HALF = C::SL / 2;
+  // LDS addresses of k-tile s's Q and P shares
+  auto qbuf = [&](int s) -> FP8MLP_LDS char* {
+    return Q3 ? smem + (s % 3) * C::Q_BYTES : smem + (s & 1) * C::STAGE_BYTES;
+  };
+  auto pbuf = [&](int s) -> FP8MLP_LDS char* {
+    return Q3 ? smem + 3 * C::Q_BYTES + (s & 1) * C::P_BYTES : smem + (s & 1) * C::STAGE_BYTES + C::Q_BYTES;
+  };
 
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -697,8 +720,22 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs a, Epi epi) {
   Frag qf[HALF][C::FM], pf[HALF][C::FN];
 
   // tile 0 in LDS for everyone, then group 1 sits out one phase
-  if (KT > 0) ld.issue(smem, 0, 0, wave);
-  wait_vmcnt<0>();
+  if constexpr (Q3) {
+    // issue order Q(0), P(0), Q(1): loads complete in issue order
+    if (KT > 0) {
+      ld.issue_q(qbuf(0), 0, wave);
+      ld.issue_p(pbuf(0), 0, wave);
+    }
+    if (KT > 1) {
+      ld.issue_q(qbuf(1), 1, wave);
+      wait_vmcnt<C::Q_LOADS>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  } else {
+    if (KT > 0) ld.issue(smem, 0, 0, wave);
+    wait_vmcnt<0>();
+  }
   __syncthreads();
   if (g == 1) __syncthreads();
 
@@ -706,8 +743,8 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs a, Epi epi) {
     const int s = j >> 1, half = j & 1;
     // ---- M(j)
     {
-      const FP8MLP_LDS char* sq = smem + (s & 1) * C::STAGE_BYTES;
-      const FP8MLP_LDS char* sp = sq + C::Q_BYTES;
+      const FP8MLP_LDS char* sq = qbuf(s);
+      const FP8MLP_LDS char* sp = pbuf(s);
 #pragma unroll
       for (int k = 0; k < HALF; k++) {
 #pragma unroll
@@ -715,10 +752,22 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs a, Epi epi) {
 #pragma unroll
         for (int fn = 0; fn < C::FN; fn++) pf[k][fn] = fr.p(sp, half * HALF + k, fn);
       }
-      if (half == 0) {
-        if (s + 1 < KT) ld.issue(smem, s + 1, (s + 1) & 1, wave);
+      if constexpr (Q3) {
+        // P(s+1), then Q(s+2); at the second half everything but Q(s+2) is in
+        if (half == 0) {
+          if (s + 1 < KT) ld.issue_p(pbuf(s + 1), s + 1, wave);
+          if (s + 2 < KT) ld.issue_q(qbuf(s + 2), s + 2, wave);
+        } else if (s + 2 < KT) {
+          wait_vmcnt<C::Q_LOADS>();
+        } else {
+          wait_vmcnt<0>();
+        }
       } else {
-        wait_vmcnt<0>();
+        if (half == 0) {
+          if (s + 1 < KT) ld.issue(smem, s + 1, (s + 1) & 1, wave);
+        } else {
+          wait_vmcnt<0>();
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);

@@ -14,11 +14,12 @@
 
 namespace fp8mlp {
 
-// dY [M,d] . W2t [h,d]^T: 256 x 256 tiles, two groups of four waves.
-using CfgDpost = GemmCfg<2, 256, 256, 128, 2, 1, KC, KC, 0, 8>;
+// dY [M,d] . W2t [h,d]^T: 256 x 256 tiles, two groups of four waves, dY
+// loaded two k-tiles ahead (three dY buffers).
+using CfgDpost = GemmCfg<2, 256, 256, 128, 2, 1, KC, KC, 0, 8, 0, 3>;
 // dpre [M,h] . W1t [d,h]^T: 192 x 256 tiles (d = 768 is three of them, and
-// M = 49152 gives exactly three rounds of 256 blocks).
-using CfgDx = GemmCfg<2, 192, 256, 128, 2, 1, KC, KC, 0, 8>;
+// M = 49152 gives exactly three rounds of 256 blocks); three dpre buffers.
+using CfgDx = GemmCfg<2, 192, 256, 128, 2, 1, KC, KC, 0, 8, 0, 3>;
 // dpre^T . X and dY^T . post: both operands are row-contiguous with k = token;
 // 256 x 256 tiles, two groups of four waves.
 using CfgDw = GemmCfg<2, 256, 256, 128, 2, 1, MNC, MNC, 0, 8>;
