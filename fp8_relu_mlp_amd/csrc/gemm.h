@@ -1,10 +1,15 @@
 // Templated MFMA GEMM core for gfx950 (CDNA4), shared by every contraction of
 // the MLP path.
 //
-// C[m][n] = sum_k A[m][k] * B[k][n], fp32 accumulation, one 256-thread block
-// (4 waves of 64, 2 x 2) per BM x BN output tile.  Blocks are sized so that
-// OCC of them fit on one CU (registers and LDS), which lets one block's
-// epilogue and barrier waits overlap another block's MFMAs.
+// C[m][n] = sum_k A[m][k] * B[k][n], fp32 accumulation, one block per BM x BN
+// output tile, in one of two kernels:
+//   gemm_kernel     256 threads (4 waves of 64, 2 x 2); OCC blocks fit on one
+//                   CU (registers and LDS), so one block's epilogue and
+//                   barrier waits overlap another block's MFMAs.
+//   gemm_pp_kernel  512 threads in two groups of four waves, one block per
+//                   CU; the groups take turns between fragment reads / global
+//                   loads and MFMAs.  With QB == 3 the Q operand has three
+//                   LDS buffers and is loaded two k-tiles ahead.
 //
 // Operand naming follows the MFMA: the MFMA "A" operand holds rows p and is fed
 // with the GEMM's B matrix (P[n][k]); the MFMA "B" operand holds columns q and
@@ -21,7 +26,8 @@
 // tails).  KC tiles are read by ds_read_b128, MNC tiles by the CDNA4
 // transposing reads ds_read_b64_tr_b16 (bf16) / ds_read_b64_tr_b8 (fp8), so no
 // operand is ever transposed in registers.  A tile holds RB bytes of k per
-// row; STAGES tiles are in flight.
+// row; STAGES tiles (two for the two-group kernel, with QB Q buffers) are in
+// flight.
 //
 // bf16 uses v_mfma_f32_32x32x16_bf16; fp8 (OCP e4m3) uses
 // v_mfma_scale_f32_32x32x64_f8f6f4 with unit (E8M0 127) block scales.
@@ -754,13 +760,14 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs a, Epi epi) {
       }
       if constexpr (Q3) {
         // P(s+1), then Q(s+2); at the second half everything but Q(s+2) is in
+        // B share of k-tile s + 1 in the first memory phase; the A share of
+        // k-tile s + 2 in the second, once k-tile s + 1 is in (two bursts of
+        // loads per k-tile instead of one keep the load queues from filling)
         if (half == 0) {
           if (s + 1 < KT) ld.issue_p(pbuf(s + 1), s + 1, wave);
-          if (s + 2 < KT) ld.issue_q(qbuf(s + 2), s + 2, wave);
-        } else if (s + 2 < KT) {
-          wait_vmcnt<C::Q_LOADS>();
         } else {
           wait_vmcnt<0>();
+          if (s + 2 < KT) ld.issue_q(qbuf(s + 2), s + 2, wave);
         }
       } else {
         if (half == 0) {

@@ -21,10 +21,10 @@ using CfgDpost = GemmCfg<2, 256, 256, 128, 2, 1, KC, KC, 0, 8, 0, 3>;
 // M = 49152 gives exactly three rounds of 256 blocks); three dpre buffers.
 using CfgDx = GemmCfg<2, 192, 256, 128, 2, 1, KC, KC, 0, 8, 0, 3>;
 // dpre^T . X and dY^T . post: both operands are row-contiguous with k = token;
-// 256 x 256 tiles, two groups of four waves.
-using CfgDw = GemmCfg<2, 256, 256, 128, 2, 1, MNC, MNC, 0, 8>;
+// 256 x 256 tiles, two groups of four waves, three buffers for the A operand.
+using CfgDw = GemmCfg<2, 256, 256, 128, 2, 1, MNC, MNC, 0, 8, 0, 3>;
 // dY^T . dec(post_q): the same tiles with the e4m3 codes as the P operand.
-using CfgDw2q = GemmCfg<2, 256, 256, 128, 2, 1, MNC, MNC, 0, 8, 1>;
+using CfgDw2q = GemmCfg<2, 256, 256, 128, 2, 1, MNC, MNC, 0, 8, 1, 3>;
 
 struct BwdPlan {
   size_t dpre_bytes, wt_bytes, part_bytes;   // dpre; W1t + W2t; split-k partials of dW
