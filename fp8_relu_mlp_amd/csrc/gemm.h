@@ -686,6 +686,12 @@ __global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) 
 // 4s-1 .. 4s+2 (group 0 runs C(j) in phase 2j, group 1 in phase 2j+1); tile
 // s+1 goes into the other LDS buffer from phase 4s-1 on and is complete,
 // for every wave, at the barrier that ends phase 4s+2.
+// With three Q buffers (QB == 3) the loads of a k-tile leave in two bursts:
+// M(2s) issues the P share of tile s+1 (into the P buffer of tile s-1), and
+// M(2s+1), after waiting for everything issued so far (tile s+1 complete),
+// issues the Q share of tile s+2 (into the Q buffer of tile s-1).  Tile s-1
+// was last read in phase 4s-2 and the earliest of these issues is in phase
+// 4s-1 (group 0's M(2s)), so both buffers are free by then.
 template <class C, class Epi, int KID>
 __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs a, Epi epi) {
   static_assert(C::NW == 8 && C::STAGES == 2 && C::REG == 0 && C::OCC == 1, "two-group kernel");
@@ -759,7 +765,6 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs a, Epi epi) {
         for (int fn = 0; fn < C::FN; fn++) pf[k][fn] = fr.p(sp, half * HALF + k, fn);
       }
       if constexpr (Q3) {
-        // P(s+1), then Q(s+2); at the second half everything but Q(s+2) is in
         // B share of k-tile s + 1 in the first memory phase; the A share of
         // k-tile s + 2 in the second, once k-tile s + 1 is in (two bursts of
         // loads per k-tile instead of one keep the load queues from filling)
