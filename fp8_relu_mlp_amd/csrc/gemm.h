@@ -46,7 +46,7 @@ enum { KC = 0, MNC = 1 };
 // symbol, which profilers report per symbol.
 enum : int {
   KID_UP = 1, KID_DOWN8, KID_DOWN_BF16, KID_DPOST, KID_DX, KID_DW1, KID_DW2, KID_LINEAR, KID_UP8,
-  KID_CE_STATS, KID_CE_GRAD, KID_CE_DX, KID_CE_DW, KID_CE8_STATS, KID_CE8_GRAD
+  KID_CE_STATS, KID_CE_GRAD, KID_CE_DX, KID_CE_DW, KID_CE8_STATS, KID_CE8_GRAD, KID_DW
 };
 
 template <int ELT_, int BM_, int BN_, int RB_, int STAGES_, int OCC_, int QL_, int PL_, int REG_ = 0, int NW_ = 4,
@@ -307,10 +307,10 @@ struct TilePos {
   int64_t m0, n0, kb, ke;
 };
 template <class C>
-__device__ __forceinline__ TilePos tile_pos(const GemmArgs& a) {
+__device__ __forceinline__ TilePos tile_pos(const GemmArgs& a, int b, int nblocks) {
   TilePos t;
   const int GROUP_M = a.group_m;
-  int i = xcd_remap(blockIdx.x, gridDim.x);
+  int i = xcd_remap(b, nblocks);
   const int per_split = a.tiles_m * a.tiles_n;
   t.split = i / per_split;
   i -= t.split * per_split;
@@ -325,6 +325,10 @@ __device__ __forceinline__ TilePos tile_pos(const GemmArgs& a) {
   t.ke = min(a.K, t.kb + a.k_per_split);
   t.KT = (int)((t.ke - t.kb + C::BK - 1) / C::BK);
   return t;
+}
+template <class C>
+__device__ __forceinline__ TilePos tile_pos(const GemmArgs& a) {
+  return tile_pos<C>(a, blockIdx.x, gridDim.x);
 }
 
 // Global -> LDS loads of the two operand tiles: buffer resources anchored at
@@ -692,21 +696,24 @@ __global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) 
 // issues the Q share of tile s+2 (into the Q buffer of tile s-1).  Tile s-1
 // was last read in phase 4s-2 and the earliest of these issues is in phase
 // 4s-1 (group 0's M(2s)), so both buffers are free by then.
-template <class C, class Epi, int KID>
-__global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs a, Epi epi) {
+template <class C, class Epi>
+constexpr int pp_smem_bytes() {
+  constexpr int EPI_BYTES = Epi::template lds_bytes<C>();
+  return C::LDS_BYTES > EPI_BYTES ? C::LDS_BYTES : EPI_BYTES;
+}
+
+// One tile (block b of nblocks in the tile order of a) of the two-group kernel.
+template <class C, class Epi>
+__device__ __forceinline__ void pp_tile(const GemmArgs& a, Epi& epi, FP8MLP_LDS char* smem, int b, int nblocks) {
   static_assert(C::NW == 8 && C::STAGES == 2 && C::REG == 0 && C::OCC == 1, "two-group kernel");
   static_assert(C::SL % 2 == 0, "k-slices split into two phases");
+  static_assert(pp_smem_bytes<C, Epi>() <= 160 * 1024, "LDS with the epilogue's staging");
   constexpr bool Q3 = C::QB == 3;
-  constexpr int EPI_BYTES = Epi::template lds_bytes<C>();
-  constexpr int SMEM = C::LDS_BYTES > EPI_BYTES ? C::LDS_BYTES : EPI_BYTES;
-  static_assert(SMEM <= 160 * 1024, "LDS with the epilogue's staging");
-  __shared__ __attribute__((aligned(1024))) char smem_raw[SMEM];
-  FP8MLP_LDS char* smem = (FP8MLP_LDS char*)smem_raw;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = wave >> 2, wm = (wave >> 1) & 1, wn = 2 * (wave & 1) + g;
   side_amax(a, wave, lane);
-  const TilePos t = tile_pos<C>(a);
+  const TilePos t = tile_pos<C>(a, b, nblocks);
   const int KT = t.KT;
   TileLoads<C> ld;
   ld.init(a, t, wave, lane);
@@ -801,6 +808,28 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs a, Epi epi) {
 
   TileCtx ctx{t.m0, t.n0, t.tm, t.tn, t.split, wm, wn, lane, a.M, a.N};
   epi.template run<C>(ctx, acc, smem);
+}
+
+template <class C, class Epi, int KID>
+__global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs a, Epi epi) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[pp_smem_bytes<C, Epi>()];
+  pp_tile<C>(a, epi, (FP8MLP_LDS char*)smem_raw, blockIdx.x, gridDim.x);
+}
+
+// Two problems of one configuration and epilogue type in one launch: blocks
+// [0, n0) run a0's tiles, blocks [off1, gridDim.x) run a1's; off1 is n0
+// rounded up to a multiple of 8, so that block b of either problem runs on
+// XCD b % 8 as the XCD-aware tile order assumes (blocks n0 .. off1 - 1 exit).
+template <class C, class Epi, int KID>
+__global__ void __launch_bounds__(512, 1) gemm_pp_kernel2(GemmArgs a0, Epi e0, GemmArgs a1, Epi e1, int n0,
+                                                          int off1) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[pp_smem_bytes<C, Epi>()];
+  const int b = blockIdx.x;
+  if (b < off1) {
+    if (b < n0) pp_tile<C>(a0, e0, (FP8MLP_LDS char*)smem_raw, b, n0);
+  } else {
+    pp_tile<C>(a1, e1, (FP8MLP_LDS char*)smem_raw, b - off1, (int)gridDim.x - off1);
+  }
 }
 
 // ------------------------------------------------------------------ epilogue helpers

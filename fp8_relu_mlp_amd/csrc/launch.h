@@ -36,6 +36,7 @@ inline const char* kid_name(int kid) {
     case KID_CE_DW: return "ce_dw_gemm";
     case KID_CE8_STATS: return "ce_head_gemm_e4m3_stats";
     case KID_CE8_GRAD: return "ce_head_gemm_e4m3_grad";
+    case KID_DW: return "dw_gemm";
   }
   return "gemm";
 }
@@ -52,6 +53,24 @@ inline int launch_gemm(const GemmArgs& args, const Epi& epi, hipStream_t st) {
   } else {
     hipLaunchKernelGGL((gemm_kernel<C, Epi, KID>), dim3((unsigned)blocks), dim3(C::NT), 0, st, a, epi);
   }
+  return launch_status();
+}
+
+// Two problems of one two-group configuration in one launch (gemm_pp_kernel2).
+template <class C, int KID, class Epi>
+inline int launch_gemm2(const GemmArgs& args0, const Epi& epi0, const GemmArgs& args1, const Epi& epi1,
+                        hipStream_t st) {
+  static_assert(C::NW == 8, "the two-group kernel");
+  const int64_t n0 = (int64_t)args0.tiles_m * args0.tiles_n * args0.splits;
+  const int64_t n1 = (int64_t)args1.tiles_m * args1.tiles_n * args1.splits;
+  if (n0 == 0 && n1 == 0) return FP8MLP_OK;
+  const int64_t off1 = (n0 + 7) / 8 * 8;
+  GemmArgs a0 = args0, a1 = args1;
+  a0.group_m = tile_group_m(a0.tiles_m, a0.tiles_n, C::OCC);
+  a1.group_m = tile_group_m(a1.tiles_m, a1.tiles_n, C::OCC);
+  TraceScope trace(kid_name(KID), st);
+  hipLaunchKernelGGL((gemm_pp_kernel2<C, Epi, KID>), dim3((unsigned)(off1 + n1)), dim3(C::NT), 0, st, a0, epi0, a1,
+                     epi1, (int)n0, (int)off1);
   return launch_status();
 }
 

@@ -27,7 +27,7 @@ using CfgDw = GemmCfg<2, 256, 256, 128, 2, 1, MNC, MNC, 0, 8, 0, 3>;
 using CfgDw2q = GemmCfg<2, 256, 256, 128, 2, 1, MNC, MNC, 0, 8, 1, 3>;
 
 struct BwdPlan {
-  size_t dpre_bytes, wt_bytes, part_bytes;   // dpre; W1t + W2t; split-k partials of dW
+  size_t dpre_bytes, wt_bytes, part_bytes;   // dpre; W1t + W2t; split-k partials of dW1 and dW2
   int splits;
   int64_t k_per_split;
 };
@@ -45,7 +45,8 @@ static BwdPlan bwd_plan(int64_t M, int64_t d, int64_t h) {
   p.k_per_split = cdiv(cdiv(M, s), 64) * 64;
   if (p.k_per_split == 0) p.k_per_split = 64;
   p.splits = (int)(M > 0 ? cdiv(M, p.k_per_split) : 1);
-  p.part_bytes = p.splits > 1 ? align_up((size_t)p.splits * (size_t)(h * d) * 4, 256) : 0;
+  // the partials of dW1, then those of dW2
+  p.part_bytes = p.splits > 1 ? 2 * align_up((size_t)p.splits * (size_t)(h * d) * 4, 256) : 0;
   return p;
 }
 
@@ -116,6 +117,36 @@ __global__ void __launch_bounds__(256) k_fill_zero(float4* __restrict__ out, int
     out[i] = float4{0.f, 0.f, 0.f, 0.f};
 }
 
+// Two reductions of the same shape in one launch (blockIdx.y picks the pair).
+__global__ void __launch_bounds__(256) k_splitk_reduce2(const float4* __restrict__ part0, float4* __restrict__ out0,
+                                                        const float4* __restrict__ part1, float4* __restrict__ out1,
+                                                        int splits, int64_t n4, int accumulate) {
+  const float4* part = blockIdx.y ? part1 : part0;
+  float4* out = blockIdx.y ? out1 : out0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    float4 a = accumulate ? out[i] : float4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < splits; s++) {
+      const float4 v = part[s * n4 + i];
+      a.x += v.x;
+      a.y += v.y;
+      a.z += v.z;
+      a.w += v.w;
+    }
+    out[i] = a;
+  }
+}
+
+static int launch_reduce2(const float* part0, float* out0, const float* part1, float* out1, int splits, int64_t n,
+                          int accumulate, hipStream_t st) {
+  const int64_t n4 = n / 4;
+  int64_t blocks = cdiv(n4, 256);
+  if (blocks > 2048) blocks = 2048;
+  TraceScope trace("splitk_reduce", st);
+  hipLaunchKernelGGL(k_splitk_reduce2, dim3((unsigned)blocks, 2), dim3(256), 0, st, (const float4*)part0,
+                     (float4*)out0, (const float4*)part1, (float4*)out1, splits, n4, accumulate);
+  return launch_status();
+}
+
 int launch_reduce(const float* part, int splits, int64_t n, float* out, int accumulate, hipStream_t st) {
   const int64_t n4 = n / 4;
   int64_t blocks = cdiv(n4, 256);
@@ -134,23 +165,6 @@ int launch_zero(float* out, int64_t n, hipStream_t st) {
   TraceScope trace("fill_zero", st);
   hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, st, (float4*)out, n4);
   return launch_status();
-}
-
-// One weight gradient C [Mo, No] = A^T B with A [K, Mo], B [K, No] (K = tokens),
-// optionally times fp32(1 / *div_by).
-template <class C, int KID>
-static int weight_grad(const uint16_t* A, int64_t Mo, const void* B, int64_t No, int64_t K, float* out,
-                       int accumulate, const BwdPlan& plan, float* part, hipStream_t st,
-                       const float* div_by = nullptr) {
-  static_assert(C::BM == CfgDw::BM && C::BN == CfgDw::BN, "the plan's split count assumes these tiles");
-  GemmArgs a{A, Mo, B, No, Mo, No, K, (int)cdiv(Mo, C::BM), (int)cdiv(No, C::BN), plan.splits, plan.k_per_split};
-  if (plan.splits == 1) {
-    EpiF32 epi{out, No, 0, accumulate, div_by};
-    return launch_gemm<C, KID>(a, epi, st);
-  }
-  EpiF32 epi{part, No, Mo * No, 0, div_by};
-  FP8MLP_TRY(launch_gemm<C, KID>(a, epi, st));
-  return launch_reduce(part, plan.splits, Mo * No, out, accumulate, st);
 }
 
 // The two entry points differ in the dgrad epilogue and the dW2 operand.
@@ -203,12 +217,28 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* W
     EpiBf16Out epi{dX, d, 0, nullptr, 0.0f, nullptr, nullptr};
     FP8MLP_TRY(launch_gemm<CfgDx, KID_DX>(a, epi, st));
   }
-  // 3. dW1 = dpre^T X ; 4. dW2 = dY^T post  (or (dY^T dec(post_q)) / scale)
-  FP8MLP_TRY((weight_grad<CfgDw, KID_DW1>(dpre, h, X, d, M, dW1, accumulate, plan, part, st)));
-  if constexpr (Q) {
-    FP8MLP_TRY((weight_grad<CfgDw2q, KID_DW2>(dY, d, post, h, M, dW2, accumulate, plan, part, st, post_scale)));
-  } else {
-    FP8MLP_TRY((weight_grad<CfgDw, KID_DW2>(dY, d, post, h, M, dW2, accumulate, plan, part, st)));
+  // 3. dW1 = dpre^T X and 4. dW2 = dY^T post (or (dY^T dec(post_q)) / scale):
+  // C [Mo, No] = A^T B with A [M, Mo], B [M, No], split-k over the M tokens
+  // into fp32 partials (split order), reduced by one launch for both.
+  {
+    static_assert(CfgDw2q::BM == CfgDw::BM && CfgDw2q::BN == CfgDw::BN, "the plan's split count assumes these tiles");
+    GemmArgs a1{dpre, h, X, d, h, d, M, (int)cdiv(h, CfgDw::BM), (int)cdiv(d, CfgDw::BN), plan.splits,
+                plan.k_per_split};
+    GemmArgs a2{dY, d, post, h, d, h, M, (int)cdiv(d, CfgDw::BM), (int)cdiv(h, CfgDw::BN), plan.splits,
+                plan.k_per_split};
+    const bool split = plan.splits > 1;
+    float* part2 = part + (size_t)plan.splits * (size_t)(h * d);
+    const float* div2 = Q ? post_scale : nullptr;
+    const EpiF32 e1 = split ? EpiF32{part, d, h * d, 0, nullptr} : EpiF32{dW1, d, 0, accumulate, nullptr};
+    const EpiF32 e2 = split ? EpiF32{part2, h, d * h, 0, div2} : EpiF32{dW2, h, 0, accumulate, div2};
+    if constexpr (Q) {
+      FP8MLP_TRY((launch_gemm<CfgDw, KID_DW1>(a1, e1, st)));
+      FP8MLP_TRY((launch_gemm<CfgDw2q, KID_DW2>(a2, e2, st)));
+    } else {
+      // both in one launch (same tiles, same kernel)
+      FP8MLP_TRY((launch_gemm2<CfgDw, KID_DW>(a1, e1, a2, e2, st)));
+    }
+    if (split) FP8MLP_TRY(launch_reduce2(part, dW1, part2, dW2, plan.splits, h * d, accumulate, st));
   }
   return FP8MLP_OK;
 }
