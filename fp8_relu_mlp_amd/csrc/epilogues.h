@@ -290,9 +290,11 @@ struct EpiBf16Out {
 
 // Backward dgrad epilogue ("NanoGPT Speedrun (Track 1)", "Changes vs Record
 // #83" item 4: relu(pre) is rebuilt from the stored post as sqrt(post)):
-//   dpre = bf16(2 * sqrt(post) * dpost),  dpost = the accumulator
-// The post tile is brought into LDS in row order, combined there with the
-// accumulators in place, and dpre leaves in row order.
+//   dpre = bf16(2 * sqrt(post) * dpost)
+// The GEMM runs on the doubled transposed W2, so the accumulator already
+// holds 2 dpost exactly and dpre = bf16(sqrt(post) * acc).  The post tile is
+// brought into LDS in row order, combined there with the accumulators in
+// place, and dpre leaves in row order.
 struct EpiDpre {
   const uint16_t* post;
   uint16_t* dpre;
@@ -325,7 +327,7 @@ struct EpiDpre {
         for (int i = 0; i < 8; i++) {
           // v_sqrt_f32 (within 1 ulp of fp32) is far below the bf16 rounding of dpre
           const float r0 = __builtin_amdgcn_sqrtf(bf16_lo(pw[i])), r1 = __builtin_amdgcn_sqrtf(bf16_hi(pw[i]));
-          o[i] = pack_bf16x2((2.0f * r0) * acc[fm][fn][2 * i], (2.0f * r1) * acc[fm][fn][2 * i + 1]);
+          o[i] = pack_bf16x2(r0 * acc[fm][fn][2 * i], r1 * acc[fm][fn][2 * i + 1]);
         }
         *p0 = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
         *p1 = i32x4{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
@@ -369,7 +371,8 @@ struct Tile8 {
 // implementation-note bullet on the BF16 post staying materialised and the
 // separate submission that drops it):
 //   post_hat = fp32(dec(post_q) * fp32(1 / *post_scale))
-//   dpre     = bf16(2 * sqrt(post_hat) * dpost),  dpost = the accumulator
+//   dpre     = bf16(2 * sqrt(post_hat) * dpost) = bf16(sqrt(post_hat) * acc),
+// acc = 2 dpost exactly (the GEMM runs on the doubled transposed W2).
 // The code tile comes into LDS in row order; each lane reads the 16 codes of
 // a fragment with one 16-byte read, keeps its dpre values in registers until
 // every wave has read its codes, then the bf16 tile is staged over the same
@@ -410,7 +413,7 @@ struct EpiDpreQ {
             const int e = 4 * w + 2 * i;
             // v_sqrt_f32 (within 1 ulp of fp32) is far below the bf16 rounding of dpre
             const float r0 = __builtin_amdgcn_sqrtf(p[2 * i]), r1 = __builtin_amdgcn_sqrtf(p[2 * i + 1]);
-            o[fm][fn][e / 2] = pack_bf16x2((2.0f * r0) * acc[fm][fn][e], (2.0f * r1) * acc[fm][fn][e + 1]);
+            o[fm][fn][e / 2] = pack_bf16x2(r0 * acc[fm][fn][e], r1 * acc[fm][fn][e + 1]);
           }
         }
       }

@@ -57,10 +57,12 @@ inline int launch_gemm(const GemmArgs& args, const Epi& epi, hipStream_t st) {
 }
 
 // Two problems of one two-group configuration in one launch (gemm_pp_kernel2).
+// Neither may carry a side job: it would run in block 0 only.
 template <class C, int KID, class Epi>
 inline int launch_gemm2(const GemmArgs& args0, const Epi& epi0, const GemmArgs& args1, const Epi& epi1,
                         hipStream_t st) {
   static_assert(C::NW == 8, "the two-group kernel");
+  FP8MLP_REQUIRE(args0.red_in == nullptr && args1.red_in == nullptr, FP8MLP_E_ARG);
   const int64_t n0 = (int64_t)args0.tiles_m * args0.tiles_n * args0.splits;
   const int64_t n1 = (int64_t)args1.tiles_m * args1.tiles_n * args1.splits;
   if (n0 == 0 && n1 == 0) return FP8MLP_OK;

@@ -50,9 +50,11 @@ static BwdPlan bwd_plan(int64_t M, int64_t d, int64_t h) {
   return p;
 }
 
-// W1t [d, h] = W1 [h, d]^T (blockIdx.z = 0) and W2t [h, d] = W2 [d, h]^T
+// W1t [d, h] = W1 [h, d]^T (blockIdx.z = 0) and W2t [h, d] = 2 W2 [d, h]^T
 // (blockIdx.z = 1) in one launch, 64 x 64 bf16 tiles through LDS (d and h
-// are multiples of 64).
+// are multiples of 64).  Doubling a bf16 value is exact (short of overflow
+// past 3.4e38), so the dgrad GEMM on W2t accumulates exactly 2 dpost and its
+// epilogue needs no separate doubling for dpre = 2 sqrt(post) dpost.
 __global__ void __launch_bounds__(256) k_transpose_weights(const uint16_t* __restrict__ W1,
                                                            const uint16_t* __restrict__ W2, int64_t d, int64_t h,
                                                            uint16_t* __restrict__ W1t, uint16_t* __restrict__ W2t) {
@@ -69,7 +71,11 @@ __global__ void __launch_bounds__(256) k_transpose_weights(const uint16_t* __res
     const int i = threadIdx.x + it * 256;
     const int r = i >> 3, ch = i & 7;
     const uint4 v = *(const uint4*)(src + (r0 + r) * C + c0 + ch * 8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if (second) {
+#pragma unroll
+      for (int e = 0; e < 4; e++) w[e] = pack_bf16x2(2.0f * bf16_lo(w[e]), 2.0f * bf16_hi(w[e]));
+    }
 #pragma unroll
     for (int e = 0; e < 4; e++) {
       tile[ch * 8 + 2 * e][r] = (uint16_t)(w[e] & 0xffffu);
