@@ -82,26 +82,34 @@ struct EpiCeStatsT {
       dq_w = *p.w_inv;
     }
     __syncthreads();   // every wave is done with the last pipeline stage
+    // columns past V only in the last column tile
+    const bool cols_in = c.n0 + C::BN <= p.V;
 #pragma unroll
     for (int fm = 0; fm < C::FM; fm++) {
       const int r = c.wm * C::WTM + fm * 32 + (c.lane & 31);
       const int64_t m = c.m0 + r;
-      float mx = -INFINITY;
+      float mx = -INFINITY, s = 0.0f;
+      auto row_stats = [&]<bool EDGE>() {
 #pragma unroll
-      for (int fn = 0; fn < C::FN; fn++) {
+        for (int fn = 0; fn < C::FN; fn++) {
 #pragma unroll
-        for (int e = 0; e < 16; e++) {
-          const float v = softcap_f(head_logit<DEQ>(acc[fm][fn][e], dq_x, dq_w), p.c, p.inv_c);
-          acc[fm][fn][e] = v;
-          if (c.n0 + epi_col<C>(c, fn, e) < p.V) mx = fmaxf(mx, v);
+          for (int e = 0; e < 16; e++) {
+            const float v = softcap_f(head_logit<DEQ>(acc[fm][fn][e], dq_x, dq_w), p.c, p.inv_c);
+            acc[fm][fn][e] = v;
+            if (!EDGE || c.n0 + epi_col<C>(c, fn, e) < p.V) mx = fmaxf(mx, v);
+          }
         }
-      }
-      float s = 0.0f;
 #pragma unroll
-      for (int fn = 0; fn < C::FN; fn++) {
+        for (int fn = 0; fn < C::FN; fn++) {
 #pragma unroll
-        for (int e = 0; e < 16; e++)
-          if (c.n0 + epi_col<C>(c, fn, e) < p.V) s += __expf(acc[fm][fn][e] - mx);
+          for (int e = 0; e < 16; e++)
+            if (!EDGE || c.n0 + epi_col<C>(c, fn, e) < p.V) s += __expf(acc[fm][fn][e] - mx);
+        }
+      };
+      if (cols_in) {
+        row_stats.template operator()<false>();
+      } else {
+        row_stats.template operator()<true>();
       }
       // the other lane half holds the same row's other 16 columns
       const float mo = __shfl_xor(mx, 32, 64), so = __shfl_xor(s, 32, 64);
@@ -154,6 +162,7 @@ template <bool DEQ>
 struct EpiCeGradT {
   CeParams p;
   const float* lse;     // [M]
+  const float* zt;      // [M, T] target logits from pass 1
   const float* dloss;   // device scalar or nullptr (1)
   uint16_t* G;          // [M, V]
 
@@ -186,6 +195,7 @@ struct EpiCeGradT {
         if (t[j] >= p.V) t[j] = -1;
         if (t[j] >= 0) wsum += w[j];
       }
+      // every column as if no target fell in it (rows past M are not stored)
 #pragma unroll
       for (int fn = 0; fn < C::FN; fn++) {
         uint32_t pk[8];
@@ -194,20 +204,49 @@ struct EpiCeGradT {
           float gv[2];
 #pragma unroll
           for (int u = 0; u < 2; u++) {
-            const int64_t n = c.n0 + epi_col<C>(c, fn, e + u);
             const float zc = softcap_f(head_logit<DEQ>(acc[fm][fn][e + u], dq_x, dq_w), p.c, p.inv_c);
             float d = wsum * __expf(zc - l);
-#pragma unroll
-            for (int j = 0; j < kCeMaxTargets; j++) d -= (t[j] == n) ? w[j] : 0.0f;
             if (p.c != 0.0f) {
               const float q = zc * p.inv_c;
               d *= 1.0f - q * q;
             }
-            gv[u] = row_in ? g * d : 0.0f;
+            gv[u] = g * d;
           }
           pk[e / 2] = pack_bf16x2(gv[0], gv[1]);
         }
         T::put(smem, c, fm, fn, pk);
+      }
+    }
+    __syncthreads();
+    // The target columns of the tile's rows (at most kCeMaxTargets a row):
+    // the same value with the targets' weights subtracted, from the target
+    // logit pass 1 stored (the same fp32 value the accumulator gives here),
+    // written over the staged entry.
+    for (int r = threadIdx.x; r < C::BM; r += C::NT) {
+      const int64_t m = c.m0 + r;
+      if (m >= p.M) continue;
+      const float l = lse[m];
+      int32_t t[kCeMaxTargets];
+      float wsum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kCeMaxTargets; j++) {
+        t[j] = j < p.T ? p.targets[m * p.T + j] : -1;
+        if (t[j] >= p.V) t[j] = -1;
+        if (t[j] >= 0) wsum += w[j];
+      }
+#pragma unroll
+      for (int j = 0; j < kCeMaxTargets; j++) {
+        if (t[j] < c.n0 || t[j] >= c.n0 + C::BN) continue;
+        const float zc = zt[m * p.T + j];
+        float d = wsum * __expf(zc - l);
+#pragma unroll
+        for (int i = 0; i < kCeMaxTargets; i++) d -= (t[i] == t[j]) ? w[i] : 0.0f;
+        if (p.c != 0.0f) {
+          const float q = zc * p.inv_c;
+          d *= 1.0f - q * q;
+        }
+        const int col = (int)(t[j] - c.n0);
+        *(FP8MLP_LDS uint16_t*)(smem + T::off(r, col >> 3) + 2 * (col & 7)) = (uint16_t)(pack_bf16x2(g * d, 0.0f) & 0xffffu);
       }
     }
     __syncthreads();
@@ -364,7 +403,7 @@ static int ce_impl(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q,
   }
   // pass 2: the logit gradient
   {
-    EpiCeGradT<FP8> epi{p, lse, dloss, G};
+    EpiCeGradT<FP8> epi{p, lse, zt, dloss, G};
     FP8MLP_TRY((launch_gemm<CH, FP8 ? KID_CE8_GRAD : KID_CE_GRAD>(head, epi, st)));
   }
   // dX = G W
