@@ -270,18 +270,26 @@ struct EpiBf16Out {
       inv_w = *w_inv;
     }
     __syncthreads();
+    // the mode is decided once, not per value
+    auto frags = [&]<bool DEQ>() {
 #pragma unroll
-    for (int fm = 0; fm < C::FM; fm++) {
+      for (int fm = 0; fm < C::FM; fm++) {
 #pragma unroll
-      for (int fn = 0; fn < C::FN; fn++) {
-        float v[16];
+        for (int fn = 0; fn < C::FN; fn++) {
+          float v[16];
 #pragma unroll
-        for (int e = 0; e < 16; e++) v[e] = mode ? (acc[fm][fn][e] * inv_s) * inv_w : acc[fm][fn][e];
-        uint32_t w[8];
+          for (int e = 0; e < 16; e++) v[e] = DEQ ? (acc[fm][fn][e] * inv_s) * inv_w : acc[fm][fn][e];
+          uint32_t w[8];
 #pragma unroll
-        for (int i = 0; i < 8; i++) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-        T::put(smem, c, fm, fn, w);
+          for (int i = 0; i < 8; i++) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+          T::put(smem, c, fm, fn, w);
+        }
       }
+    };
+    if (mode) {
+      frags.template operator()<true>();
+    } else {
+      frags.template operator()<false>();
     }
     __syncthreads();
     T::store(smem, c, y, ld);
