@@ -457,33 +457,41 @@ struct EpiF32 {
     // fragment is wholly inside or outside the matrix
     float* base = out + (int64_t)c.split * split_stride;
     const float f = div_by ? 1.0f / *div_by : 1.0f;
+    // the two options are decided once, not per value
+    auto stores = [&]<bool DIV, bool ACC>() {
 #pragma unroll
-    for (int fm = 0; fm < C::FM; fm++) {
-      const int64_t m = c.m0 + epi_row<C>(c, fm);
-      if (m >= c.M) continue;
+      for (int fm = 0; fm < C::FM; fm++) {
+        const int64_t m = c.m0 + epi_row<C>(c, fm);
+        if (m >= c.M) continue;
 #pragma unroll
-      for (int fn = 0; fn < C::FN; fn++) {
-        if (c.n0 + epi_col<C>(c, fn, 0) >= c.N) continue;
+        for (int fn = 0; fn < C::FN; fn++) {
+          if (c.n0 + epi_col<C>(c, fn, 0) >= c.N) continue;
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-          float4* dst = (float4*)(base + m * ld + c.n0 + epi_col<C>(c, fn, 4 * g));
-          float4 v = {acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2], acc[fm][fn][4 * g + 3]};
-          if (div_by) {
-            v.x *= f;
-            v.y *= f;
-            v.z *= f;
-            v.w *= f;
+          for (int g = 0; g < 4; g++) {
+            float4* dst = (float4*)(base + m * ld + c.n0 + epi_col<C>(c, fn, 4 * g));
+            float4 v = {acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2], acc[fm][fn][4 * g + 3]};
+            if constexpr (DIV) {
+              v.x *= f;
+              v.y *= f;
+              v.z *= f;
+              v.w *= f;
+            }
+            if constexpr (ACC) {
+              const float4 o = *dst;
+              v.x += o.x;
+              v.y += o.y;
+              v.z += o.z;
+              v.w += o.w;
+            }
+            *dst = v;
           }
-          if (accumulate) {
-            const float4 o = *dst;
-            v.x += o.x;
-            v.y += o.y;
-            v.z += o.z;
-            v.w += o.w;
-          }
-          *dst = v;
         }
       }
+    };
+    if (div_by) {
+      if (accumulate) stores.template operator()<true, true>(); else stores.template operator()<true, false>();
+    } else {
+      if (accumulate) stores.template operator()<false, true>(); else stores.template operator()<false, false>();
     }
   }
 };
