@@ -50,22 +50,23 @@ static BwdPlan bwd_plan(int64_t M, int64_t d, int64_t h) {
   return p;
 }
 
-// W1t [d, h] = W1 [h, d]^T (blockIdx.z = 0) and W2t [h, d] = 2 W2 [d, h]^T
-// (blockIdx.z = 1) in one launch, 64 x 64 bf16 tiles through LDS (d and h
-// are multiples of 64).  Doubling a bf16 value is exact (short of overflow
+// W1t [d, h] = W1 [h, d]^T and W2t [h, d] = 2 W2 [d, h]^T in one launch,
+// 64 x 64 bf16 tiles through LDS (d and h are multiples of 64), one block per
+// tile.  Doubling a bf16 value is exact (short of overflow
 // past 3.4e38), so the dgrad GEMM on W2t accumulates exactly 2 dpost and its
 // epilogue needs no separate doubling for dpre = 2 sqrt(post) dpost.
 __global__ void __launch_bounds__(256) k_transpose_weights(const uint16_t* __restrict__ W1,
                                                            const uint16_t* __restrict__ W2, int64_t d, int64_t h,
                                                            uint16_t* __restrict__ W1t, uint16_t* __restrict__ W2t) {
   __shared__ uint16_t tile[64][64 + 2];   // [c][r]
-  const bool second = blockIdx.z == 1;
+  // blocks [0, n) transpose W1's (h/64) x (d/64) tiles, blocks [n, 2n) W2's
+  const int64_t n = (h / 64) * (d / 64);
+  const bool second = blockIdx.x >= n;
+  const int64_t b = second ? blockIdx.x - n : blockIdx.x;
   const uint16_t* src = second ? W2 : W1;
   uint16_t* dst = second ? W2t : W1t;
   const int64_t R = second ? d : h, C = second ? h : d;   // src is [R, C]
-  // the grid covers max(d, h) / 64 tiles in each direction; skip the excess
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  if (r0 >= R || c0 >= C) return;
+  const int64_t r0 = (b / (C / 64)) * 64, c0 = (b % (C / 64)) * 64;
 #pragma unroll
   for (int it = 0; it < 2; it++) {
     const int i = threadIdx.x + it * 256;
@@ -96,9 +97,9 @@ __global__ void __launch_bounds__(256) k_transpose_weights(const uint16_t* __res
 
 static int launch_transpose_weights(const uint16_t* W1, const uint16_t* W2, int64_t d, int64_t h, uint16_t* W1t,
                                     uint16_t* W2t, hipStream_t st) {
-  const unsigned g = (unsigned)((d > h ? d : h) / 64);
+  const unsigned blocks = (unsigned)(2 * (h / 64) * (d / 64));
   TraceScope trace("transpose_weights", st);
-  hipLaunchKernelGGL(k_transpose_weights, dim3(g, g, 2), dim3(256), 0, st, W1, W2, d, h, W1t, W2t);
+  hipLaunchKernelGGL(k_transpose_weights, dim3(blocks), dim3(256), 0, st, W1, W2, d, h, W1t, W2t);
   return launch_status();
 }
 
