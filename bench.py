@@ -73,6 +73,17 @@ def kernel_work(M, d, h):
     }
 
 
+# The bandwidth-bound kernels at the workload's large sizes, as --hbm-kernels
+# runs them: algorithmic HBM bytes per launch.
+def hbm_kernel_bytes(M, d, h):
+    return {
+        "amax_partial": M * h * 2,                  # max |x| over a [M, h] bf16 tensor (post-sized)
+        "cast_transpose": M * h * 2 + M * h,        # [M, h] bf16 -> [h, M] e4m3, given scale
+        "count_top_codes": M * h,                   # e4m3 codes at 448 in a [M, h] tensor
+        "quantize_e4m3": M * d * 2 + M * d,         # X [M, d] bf16 -> e4m3 (fp8_linear's first step)
+    }
+
+
 # launches that run more than one of the step's GEMMs
 GEMMS_PER_LAUNCH = {"dw_gemm": 2}
 
@@ -189,6 +200,36 @@ def summarize_profiles(outdir):
         fh.write("\n")
     print(f"wrote {PROFILES}/kernel_trace_mlp_fwd_bwd_M49152.md, hbm_traffic_mlp_fwd_bwd_M49152.md, {TRAFFIC_FILE}")
 
+    # bandwidth-bound kernels (optional run of --hbm-kernels under --kernel-trace)
+    if os.path.isdir(os.path.join(outdir, "hbmk")):
+        durs = {}
+        for r in rows("hbmk", "*kernel_trace.csv"):
+            n = logical_kernel_name(r["Kernel_Name"])
+            durs.setdefault(n, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        nbytes = hbm_kernel_bytes(M, D, H)
+        cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d OUT/hbmk -o k -- "
+               "python3 bench.py --hbm-kernels")
+        lines = ["# Bandwidth-bound kernels at the workload's sizes (one MI355X)", "",
+                 "Command (from a scratch directory, TMPDIR=/tmp):", "", f"    {cmd}", "",
+                 f"Sizes: M={M}, d={D}, h={H}. amax_partial: max |x| over a [M, h] bf16 tensor; cast_transpose:",
+                 "[M, h] bf16 -> [h, M] e4m3 with a given scale; count_top_codes: the e4m3 codes at 448 in a",
+                 "[M, h] tensor; quantize_e4m3: X [M, d] bf16 -> e4m3 (the first step of fp8_linear). GB/s =",
+                 f"algorithmic bytes per launch / average duration; peak HBM {PEAK_HBM / 1e3:.0f} TB/s.", "",
+                 "| kernel | launches | avg us | algorithmic MB | GB/s | of peak |", "|---|---:|---:|---:|---:|---:|"]
+        ours = set(OTHER_NAMES.values()) | set(KID_NAMES.values())
+        for n in sorted((k for k in durs if k in ours), key=lambda k: -sum(durs[k]) / len(durs[k])):
+            avg = sum(durs[n]) / len(durs[n])
+            if n in nbytes:
+                gbs = nbytes[n] / (avg * 1e-6) / 1e9
+                lines.append(f"| {n} | {len(durs[n])} | {avg:.1f} | {nbytes[n] / 1e6:.1f} | {gbs:.0f} | "
+                             f"{gbs / PEAK_HBM:.2f} |")
+            else:
+                lines.append(f"| {n} | {len(durs[n])} | {avg:.1f} |  |  |  |")
+        lines += ["", f"Kernel sources digest: `{kernel_source_hash()}`"]
+        with open(os.path.join(PROFILES, "kernel_trace_hbm_kernels_M49152.md"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        print(f"wrote {PROFILES}/kernel_trace_hbm_kernels_M49152.md")
+
     # matrix-core counters (optional run): executed MFMA work and busy share
     if os.path.isdir(os.path.join(outdir, "mfma")):
         acc = {}
@@ -265,6 +306,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip the FP8-linear / eval / ablation lines")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (scales the HBM byte counters)")
+    ap.add_argument("--hbm-kernels", action="store_true",
+                    help="only run the bandwidth-bound kernels at the workload's large sizes, 5 launches each "
+                         "(for a rocprofv3 kernel trace)")
     ap.add_argument("--summarize-profiles", metavar="OUT",
                     help="write the profiles/ summaries from the rocprofv3 runs under OUT (no GPU needed)")
     args = ap.parse_args()
@@ -294,6 +338,33 @@ def main():
 
     dev = torch.device("cuda:0")
     fm.lib()
+    if args.hbm_kernels:
+        # post-sized bf16 values >= 0, their e4m3 codes and a bf16 X, generated on the device
+        g = torch.Generator(device=dev).manual_seed(7)
+        big = torch.randn((M, H), generator=g, device=dev).square_().to(torch.bfloat16)
+        xs = torch.randn((M, D), generator=g, device=dev).to(torch.bfloat16)
+        f1 = lambda v=0.0: torch.full((1,), v, dtype=torch.float32, device=dev)
+        amx, sc, sx, xam = f1(), f1(16.0), f1(64.0), f1()
+        ws_a = torch.empty(max(1, fm.lib().amax_reduce_workspace(M * H)), dtype=torch.uint8, device=dev)
+        ws_c = torch.empty(max(1, fm.lib().fp8_cast_transpose_workspace(M, H)), dtype=torch.uint8, device=dev)
+        q = torch.empty((H, M), dtype=torch.uint8, device=dev)
+        cnt = torch.zeros(1, dtype=torch.int64, device=dev)
+        ws_t = torch.empty(max(1, fm.lib().fp8_saturation_count_workspace(M * H)), dtype=torch.uint8, device=dev)
+        wt = torch.zeros((D, D), dtype=torch.uint8, device=dev)
+        winv = f1(1.0)
+        yl = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+        ws_l = torch.empty(max(1, fm.lib().fp8_linear_workspace(M, D)), dtype=torch.uint8, device=dev)
+        for _ in range(5):
+            fm.amax_reduce(big, amx, workspace=ws_a)
+        for _ in range(5):
+            fm.fp8_cast_transpose(big, q, scale_in=sc, workspace=ws_c)
+        for _ in range(5):
+            fm.fp8_saturation_count(q, cnt, workspace=ws_t)
+        for _ in range(5):
+            fm.fp8_linear(xs, sx, wt, winv, yl, x_amax_out=xam, workspace=ws_l)
+        torch.cuda.synchronize()
+        print(json.dumps({"bytes_per_launch": hbm_kernel_bytes(M, D, H), "launches": 5}))
+        return
     log("generating inputs")
     ins = synth.mlp_inputs(M, D, H, synth.WORKLOADS["fwdbwd"][3], with_dy=True)
 
