@@ -121,6 +121,28 @@ def test_ce_missing_and_out_of_range_targets(fm):
     check(dict(ins, targets=ref_t), g, [0.7, 0.3], 15.0)
 
 
+def test_ce_duplicate_targets(fm):
+    # Rows whose successive targets repeat a token: the gradient at that
+    # column carries the sum of their weights.  Checked entry by entry at
+    # every target column (a bf16 value, so within a few bf16 ulps of the
+    # fp64 oracle), and as a whole by check().
+    case("ce duplicate targets")
+    ins = synth.ce_inputs(256, 128, 512, 3, 84)
+    t = ins["targets"]
+    t[::3, 1] = t[::3, 0]
+    t[1::4, 2] = t[1::4, 0]
+    t[2::5, 2] = t[2::5, 1]
+    w = [1.0, 0.5, 0.25]
+    g = run(fm, ins, w, 15.0)
+    ref = check(ins, g, w, 15.0)
+    Gg = F.bf16_to_f64(g["G"])
+    rows = np.repeat(np.arange(t.shape[0]), t.shape[1])
+    cols = t.reshape(-1)
+    ok = cols >= 0
+    a, b = Gg[rows[ok], cols[ok]], ref["G"][rows[ok], cols[ok]]
+    assert (np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 1e-9).all(), np.abs(a - b).max()
+
+
 def test_ce_accumulate(fm):
     case("ce accumulate")
     ins = synth.ce_inputs(384, 128, 512, 2, 84)
