@@ -693,7 +693,8 @@ __global__ void __launch_bounds__(256, C::OCC) gemm_kernel(GemmArgs a, Epi epi) 
 // With three Q buffers (QB == 3) the loads of a k-tile leave in two bursts:
 // M(2s) issues the P share of tile s+1 (into the P buffer of tile s-1), and
 // M(2s+1), after waiting for everything issued so far (tile s+1 complete),
-// issues the Q share of tile s+2 (into the Q buffer of tile s-1).  Tile s-1
+// issues the Q share of tile s+2 (into the Q buffer of tile s-1).  Before the
+// loop only tile 0 is loaded; tile 1's Q share goes out in M(0).  Tile s-1
 // was last read in phase 4s-2 and the earliest of these issues is in phase
 // 4s-1 (group 0's M(2s)), so both buffers are free by then.
 template <class C, class Epi>
@@ -740,17 +741,13 @@ __device__ __forceinline__ void pp_tile(const GemmArgs& a, Epi& epi, FP8MLP_LDS 
 
   // tile 0 in LDS for everyone, then group 1 sits out one phase
   if constexpr (Q3) {
-    // issue order Q(0), P(0), Q(1): loads complete in issue order
+    // only tile 0 before the start (every block of a round issues these at
+    // once); tile 1's Q share goes out with its P share in M(0)
     if (KT > 0) {
       ld.issue_q(qbuf(0), 0, wave);
       ld.issue_p(pbuf(0), 0, wave);
     }
-    if (KT > 1) {
-      ld.issue_q(qbuf(1), 1, wave);
-      wait_vmcnt<C::Q_LOADS>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_vmcnt<0>();
   } else {
     if (KT > 0) ld.issue(smem, 0, 0, wave);
     wait_vmcnt<0>();
@@ -776,6 +773,7 @@ __device__ __forceinline__ void pp_tile(const GemmArgs& a, Epi& epi, FP8MLP_LDS 
         // k-tile s + 2 in the second, once k-tile s + 1 is in (two bursts of
         // loads per k-tile instead of one keep the load queues from filling)
         if (half == 0) {
+          if (s == 0 && KT > 1) ld.issue_q(qbuf(1), 1, wave);
           if (s + 1 < KT) ld.issue_p(pbuf(s + 1), s + 1, wave);
         } else {
           wait_vmcnt<0>();
