@@ -17,13 +17,13 @@
 
 namespace fp8mlp {
 
-// The bf16 GEMMs keep three LDS buffers for their A operand (loaded two
-// k-tiles ahead); the e4m3 head keeps two.
+// Every two-group GEMM here keeps three LDS buffers for its A operand
+// (loaded two k-tiles ahead).
 // X [M,d] . W [V,d]^T: both k-contiguous, two groups of four waves.
 using CfgCeHead = GemmCfg<2, 256, 256, 128, 2, 1, KC, KC, 0, 8, 0, 3>;
 // The FP8 form: Xq [M,d] . Wt_q [d,V] (the transposed e4m3 cache, read with
 // transposing LDS loads).
-using CfgCeHead8 = GemmCfg<1, 256, 256, 128, 2, 1, KC, MNC, 0, 8>;
+using CfgCeHead8 = GemmCfg<1, 256, 256, 128, 2, 1, KC, MNC, 0, 8, 0, 3>;
 // G [M,V] . W [V,d]: G k-contiguous, W row-contiguous (k = vocabulary row).
 using CfgCeDx = GemmCfg<2, 192, 256, 128, 2, 1, KC, MNC, 0, 8, 0, 3>;
 // G^T . X: both row-contiguous with k = token.

@@ -12,8 +12,9 @@ using CfgUp = GemmCfg<2, 256, 256, 128, 2, 1, KC, KC, 0, 8, 0, 3>;
 // post_q [M,h] . W2t_q [h,d] : e4m3, the cache is read with transposing LDS loads.
 using CfgDown8 = GemmCfg<1, 192, 128, 128, 2, 2, KC, MNC>;
 // Xq [M,d] . W1t_q [d,h] : the up-projection in e4m3 (the W1 cache is read
-// with transposing LDS loads), 256 x 256 tiles, two groups of four waves.
-using CfgUp8 = GemmCfg<1, 256, 256, 128, 2, 1, KC, MNC, 0, 8>;
+// with transposing LDS loads), 256 x 256 tiles, two groups of four waves,
+// three Xq buffers.
+using CfgUp8 = GemmCfg<1, 256, 256, 128, 2, 1, KC, MNC, 0, 8, 0, 3>;
 // post [M,h] . W2[d,h]^T : bf16 eval path; the same shape as the backward's
 // dX GEMM, on the same 192 x 256 two-group tiles with three post buffers.
 using CfgDownBf16 = GemmCfg<2, 192, 256, 128, 2, 1, KC, KC, 0, 8, 0, 3>;
