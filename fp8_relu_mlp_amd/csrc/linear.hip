@@ -79,6 +79,8 @@ int fp8_linear(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, con
                size_t workspace_bytes, void* stream) {
   FP8MLP_REQUIRE(M >= 0 && K > 0 && N > 0 && K % 128 == 0 && N % 64 == 0, FP8MLP_E_SHAPE);
   FP8MLP_REQUIRE(x_scale && w_inv_scale && Wt_q, FP8MLP_E_NULL);
+  // block 0 of the GEMM writes x_amax_out while its other blocks read the scales
+  FP8MLP_REQUIRE(x_amax_out != x_scale && x_amax_out != w_inv_scale, FP8MLP_E_ARG);
   if (M > 0) FP8MLP_REQUIRE(X && Y, FP8MLP_E_NULL);
   for (const void* p : {(const void*)X, (const void*)Wt_q, (const void*)Y})
     FP8MLP_REQUIRE(p == nullptr || aligned16(p), FP8MLP_E_ALIGN);

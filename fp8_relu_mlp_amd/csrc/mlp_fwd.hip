@@ -57,6 +57,9 @@ int mlp_relu2_fwd(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t
   if (M > 0) FP8MLP_REQUIRE(X && W1 && Y && (post || train), FP8MLP_E_NULL);
   if (train) {
     FP8MLP_REQUIRE(amax_prev != nullptr, FP8MLP_E_NULL);
+    // block 0 of the down-projection writes amax_out / scale_out while later
+    // blocks still read amax_prev: the three must be distinct words
+    FP8MLP_REQUIRE(amax_out != amax_prev && scale_out != amax_prev && scale_out != amax_out, FP8MLP_E_ARG);
     if (M > 0) FP8MLP_REQUIRE(W2t_q && w2_inv_scale && post_q, FP8MLP_E_NULL);
     FP8MLP_REQUIRE(margin > 0.0f && margin <= 3.4e38f, FP8MLP_E_ARG);
   } else if (M > 0) {
@@ -126,6 +129,13 @@ int mlp_relu2_fwd_fp8up(const uint16_t* X, const float* x_scale, const uint8_t* 
   FP8MLP_REQUIRE(x_scale && W1t_q && w1_inv_scale && W2t_q && w2_inv_scale && amax_prev && amax_out, FP8MLP_E_NULL);
   if (M > 0) FP8MLP_REQUIRE(X && post_q && Y, FP8MLP_E_NULL);
   FP8MLP_REQUIRE(margin > 0.0f && margin <= 3.4e38f, FP8MLP_E_ARG);
+  // amax_out / scale_out are written by block 0 of the down-projection while
+  // later blocks still read amax_prev; x_amax_out by block 0 of the
+  // up-projection while its other blocks read x_scale
+  FP8MLP_REQUIRE(amax_out != amax_prev && scale_out != amax_prev && scale_out != amax_out, FP8MLP_E_ARG);
+  FP8MLP_REQUIRE(x_amax_out == nullptr || (x_amax_out != x_scale && x_amax_out != amax_prev &&
+                                           x_amax_out != amax_out && x_amax_out != scale_out),
+                 FP8MLP_E_ARG);
   for (const void* p : {(const void*)X, (const void*)W1t_q, (const void*)W2t_q, (const void*)post,
                         (const void*)post_q, (const void*)Y})
     FP8MLP_REQUIRE(p == nullptr || aligned16(p), FP8MLP_E_ALIGN);

@@ -99,6 +99,10 @@ int fp8mlp_last_hip_error(void);
  *   amax_prev: device fp32, amax_out of the previous step.  margin: the
  *   safety margin (> 0, finite; 2 in the speedrun workload).
  *   amax_out: device fp32, required.  scale_out: device fp32 or NULL.
+ *   In TRAIN mode amax_prev, amax_out and scale_out must be three distinct
+ *   words (E_ARG otherwise): the launch writes amax_out and scale_out while
+ *   it still reads amax_prev, so amax_t and amax_{t-1} need two buffers
+ *   (swap them between steps).
  *   workspace: device memory of mlp_relu2_fwd_workspace(M, d, h) bytes.
  * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_ARCH, E_ARG, E_HIP.
  * ---------------------------------------------------------------------- */
@@ -222,7 +226,8 @@ int fp8_saturation_count(const uint8_t* q, int64_t n, uint64_t* count_out, void*
  *   Y  = bf16((Xq . Wt_q) * fp32(1 / *x_scale) * *w_inv_scale)
  * X [M, K] bf16, Wt_q [K, N] e4m3 (from fp8_cast_transpose), Y [M, N] bf16.
  * x_scale, w_inv_scale: device fp32.  x_amax_out: device fp32 or NULL; if
- * given it receives max |X| (for the next step's delayed scale).
+ * given it receives max |X| (for the next step's delayed scale); it must not
+ * be x_scale or w_inv_scale (E_ARG), which the same launch still reads.
  * K: a positive multiple of 128, N: a positive multiple of 64; M >= 0.
  * workspace: fp8_linear_workspace(M, K) bytes (the e4m3 copy of X and the
  * conversion's per-block maxima of |X|).
@@ -248,7 +253,9 @@ int fp8_linear(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, con
  * Arguments: X [M, d] bf16; W1t_q [d, h] e4m3, the transposed W1 cache
  * (fp8_cast_transpose of W1 [h, d]) with its dequantisation multiplier
  * w1_inv_scale; W2t_q / w2_inv_scale as in mlp_relu2_fwd.  x_amax_out:
- * device fp32 or NULL; if given it receives max |X|.  d and h: multiples of
+ * device fp32 or NULL; if given it receives max |X|.  amax_prev, amax_out,
+ * scale_out and x_amax_out must be distinct words, and x_amax_out must not
+ * be x_scale (E_ARG otherwise; see mlp_relu2_fwd).  d and h: multiples of
  * 128; M >= 0.  workspace: mlp_relu2_fwd_fp8up_workspace(M, d, h) bytes
  * (the partial amax tensor, per-block maxima of |X| and the e4m3 copy of X;
  * 0 for M = 0).  The backward is

@@ -4,6 +4,12 @@
 * the Python binding declares exactly those functions;
 * workspace queries and argument validation (which runs on the host before
   any device call) return the documented status codes.
+
+The validation tests pass small integers as device addresses: they rely on
+the library rejecting the call before it touches a device.  On a host where a
+GPU is visible a regression in the order of the checks could launch a kernel
+on such an address, so those tests skip themselves there (the `L_nogpu`
+fixture); the load / export checks run everywhere.
 """
 import ctypes
 import os
@@ -30,6 +36,24 @@ def L():
         pytest.fail("libfp8mlp.so is not built (run __graft_entry__.build())")
     from fp8_relu_mlp_amd import _lib
     return _lib.lib()
+
+
+def _gpu_visible():
+    """A GPU is visible to this process (device_count does not initialise HIP)."""
+    if os.environ.get("HIP_VISIBLE_DEVICES") == "-1":
+        return False
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return os.path.exists("/dev/kfd")
+
+
+@pytest.fixture(scope="module")
+def L_nogpu(L):
+    if _gpu_visible():
+        pytest.skip("fake device addresses are passed to the library: not run where a GPU is visible")
+    return L
 
 
 def test_header_declares_the_boundary():
@@ -68,14 +92,15 @@ def test_workspace_sizes(L):
 
 
 def _fwd(L, **kw):
-    args = dict(mode=0, X=16, W1=16, W2t_q=16, w2_inv=16, W2=None, amax_prev=16, margin=2.0, post=16,
-                post_q=16, amax_out=16, scale_out=None, Y=16, M=256, d=128, h=512, ws=16, wsb=1 << 20,
+    args = dict(mode=0, X=16, W1=16, W2t_q=16, w2_inv=16, W2=None, amax_prev=32, margin=2.0, post=16,
+                post_q=16, amax_out=48, scale_out=None, Y=16, M=256, d=128, h=512, ws=16, wsb=1 << 20,
                 stream=None)
     args.update(kw)
     return L.mlp_relu2_fwd(*args.values())
 
 
-def test_fwd_validation_before_any_device_call(L):
+def test_fwd_validation_before_any_device_call(L_nogpu):
+    L = L_nogpu
     assert _fwd(L, mode=7) == E_ARG
     assert _fwd(L, d=100) == E_SHAPE
     assert _fwd(L, h=192) == E_SHAPE            # train needs h % 128 == 0
@@ -89,9 +114,14 @@ def test_fwd_validation_before_any_device_call(L):
     assert _fwd(L, ws=None) == E_WS
     assert _fwd(L, wsb=8) == E_WS
     assert _fwd(L, mode=1, W2=None) == E_NULL   # eval needs the bf16 W2
+    # amax_t is written while amax_{t-1} is still read: no aliasing
+    assert _fwd(L, amax_out=32) == E_ARG
+    assert _fwd(L, scale_out=32) == E_ARG
+    assert _fwd(L, scale_out=48) == E_ARG
 
 
-def test_bwd_and_misc_validation(L):
+def test_bwd_and_misc_validation(L_nogpu):
+    L = L_nogpu
     b = lambda **kw: L.mlp_relu2_bwd(*dict(dict(dY=16, X=16, W1=16, W2=16, post=16, dX=16, dW1=16, dW2=16,
                                                  acc=0, M=256, d=128, h=512, ws=16, wsb=1 << 30,
                                                  stream=None), **kw).values())
@@ -116,9 +146,11 @@ def test_bwd_and_misc_validation(L):
     assert lin(Y=17) == E_ALIGN
     assert lin(ws=None) == E_WS
     assert lin(wsb=100) == E_WS
+    assert lin(am=16) == E_ARG                # x_amax_out aliases x_scale
 
 
-def test_stack_helpers_validation(L):
+def test_stack_helpers_validation(L_nogpu):
+    L = L_nogpu
     assert L.rmsnorm_fwd(16, 16, 16, 4, 100, 1e-6, None) == E_SHAPE     # d % 8
     assert L.rmsnorm_fwd(16, 16, 16, -1, 64, 1e-6, None) == E_SHAPE
     assert L.rmsnorm_fwd(16, 16, 16, 4, 64, -1.0, None) == E_ARG
@@ -134,12 +166,15 @@ def test_stack_helpers_validation(L):
     assert L.sgd_update_bf16(16, 40, 16, 1e-3, None) == E_ALIGN
 
 
-def test_variant_entry_points_validation(L):
+def test_variant_entry_points_validation(L_nogpu):
     """The e4m3 up-projection forward, the backward on the e4m3 post copy and
     the top-code count reject bad arguments before touching a device."""
+    L = L_nogpu
     ws = L.mlp_relu2_fwd_fp8up_workspace(256, 128, 256)
     assert ws >= 256 * 128 and L.mlp_relu2_fwd_fp8up_workspace(0, 128, 256) == 0
-    args = [16, 16, 16, 16, 16, 16, 16, 2.0, 16, 16, 16, 16, 16, 16]
+    # X, x_scale, W1t_q, w1_inv, W2t_q, w2_inv, amax_prev, margin, post, post_q, amax_out, scale_out, Y,
+    # x_amax_out
+    args = [16, 20, 16, 24, 16, 28, 32, 2.0, 16, 16, 36, 40, 16, 44]
     assert L.mlp_relu2_fwd_fp8up(*args, 256, 192, 256, 16, ws, None) == E_SHAPE    # d % 128
     assert L.mlp_relu2_fwd_fp8up(*args, 256, 128, 192, 16, ws, None) == E_SHAPE    # h % 128
     bad = list(args)
@@ -149,6 +184,10 @@ def test_variant_entry_points_validation(L):
     bad[7] = 0.0                                                                    # margin
     assert L.mlp_relu2_fwd_fp8up(*bad, 256, 128, 256, 16, ws, None) == E_ARG
     assert L.mlp_relu2_fwd_fp8up(*args, 256, 128, 256, 16, ws - 1, None) == E_WS
+    for i, j in ((10, 6), (11, 6), (11, 10), (13, 1), (13, 6), (13, 10)):
+        bad = list(args)
+        bad[i] = bad[j]                                                             # aliased scalars
+        assert L.mlp_relu2_fwd_fp8up(*bad, 256, 128, 256, 16, ws, None) == E_ARG, (i, j)
     wb = L.mlp_relu2_bwd_workspace(256, 128, 256)
     assert L.mlp_relu2_bwd_fp8post(16, 16, 16, 16, 16, None, 16, 16, 16, 0, 256, 128, 256, 16, wb,
                                    None) == E_NULL                                  # post_scale

@@ -1,10 +1,17 @@
 """GPU parity at the full benchmark sizes, in the launch configuration the
 benchmark times (Relu2MLP: fwd TRAIN + bwd + W2 cache refresh).
 
-The oracle checks sampled outputs it can compute one by one (rows of post,
-post_q, Y, dX; rows of dW1; columns of dW2) plus properties over whole
-tensors (amax against the max of the GPU's full post).
+At the timed workload (M=49152, d=768, h=3072) every element of post, post_q,
+Y, dX, dW1, dW2 and of the two intermediate workspaces (the forward's
+partial-amax tensor, the backward's dpre) is compared with the oracle, in
+row chunks of 4096: against the oracle run on its own from X, W1, W2 and dY
+(the gates 1e-2 / 2e-2), and, tighter, against the oracle fed the GPU's own
+intermediates.  The other tests check sampled outputs the oracle computes
+one by one, plus properties over whole tensors.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -69,6 +76,133 @@ def test_fwdbwd_full_size_sampled(fm):
     assert rel_fro(F.bf16_to_f64(bits(dX)[rows]), bs["dX_rows"]) < 4e-3
     assert rel_fro(dW1.cpu().numpy()[r1].astype(np.float64), bs["dW1_rows"]) < 4e-3
     assert rel_fro(dW2.cpu().numpy()[:, c2].astype(np.float64), bs["dW2_cols"]) < 1e-4
+
+
+class _Fro:
+    """Relative Frobenius error of a tensor compared chunk by chunk."""
+
+    def __init__(self):
+        self.num = 0.0
+        self.den = 0.0
+
+    def add(self, got, ref):
+        got = np.asarray(got, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        self.num += float(np.sum((got - ref) ** 2))
+        self.den += float(np.sum(ref ** 2))
+
+    def value(self):
+        return (self.num / max(self.den, 1e-300)) ** 0.5
+
+
+def test_fwdbwd_full_size_whole_tensors(fm):
+    """The timed workload (M=49152, d=768, h=3072, margin 2, the first step's
+    own amax as amax_prev), every output element against the oracle.
+
+    Independent chain: the oracle alone from X, W1, W2, dY -- its own post,
+    its own amax as the bootstrap amax_prev, its own e4m3 codes, Y, dpre, dX,
+    dW1, dW2 -- against the GPU: post, dX, dW1, dW2 within 1e-2, Y within
+    2e-2 (relative Frobenius over the whole tensor).
+    Given the GPU's intermediates: every post_q code bit-exact from the GPU's
+    post and scale; the partial-amax workspace bit-exact against the oracle's
+    tile maxima of the GPU's post (256 x 256 tiles); Y within 4e-3 of the
+    oracle's FP8 GEMM of the GPU's codes; dpre (the backward workspace), dX
+    and dW1 within 4e-3 and dW2 within 1e-4 of the oracle's backward fed the
+    GPU's post."""
+    M, d, h = synth.WORKLOADS["fwdbwd"][:3]
+    seed = synth.WORKLOADS["fwdbwd"][3]
+    ins = synth.mlp_inputs(M, d, h, seed, with_dy=True)
+    case(f"full-size fwd+bwd whole tensors M={M} d={d} h={h}")
+    L = fm.lib()
+    blk = fm.Relu2MLP(bf16_dev(ins["W1"]), bf16_dev(ins["W2"]), margin=2.0, amax_init=1.0)
+    X, dY = bf16_dev(ins["X"]), bf16_dev(ins["dY"])
+    ws_f = torch.zeros(L.mlp_relu2_fwd_workspace(M, d, h), dtype=torch.uint8, device=DEV)
+    ws_b = torch.zeros(L.mlp_relu2_bwd_workspace(M, d, h), dtype=torch.uint8, device=DEV)
+    blk.forward(X, workspace=ws_f)                   # bootstrap amax_prev
+    amax_prev = float(blk.amax_prev.item())
+    Y, post, post_q = blk.forward(X, workspace=ws_f)
+    dX, dW1, dW2 = blk.backward(dY, X, post, workspace=ws_b)
+    torch.cuda.synchronize()
+    BM = BN = 256
+    tm, tn = -(-M // BM), -(-h // BN)
+    part_g = ws_f[:tm * tn * 4].view(torch.float32).cpu().numpy().reshape(tm, tn)
+    dpre_g = bits(ws_b[:M * h * 2].view(torch.bfloat16).view(M, h))
+    post_g, pq_g, y_g, dx_g = bits(post), post_q.cpu().numpy(), bits(Y), bits(dX)
+    dw1_g = dW1.cpu().numpy().astype(np.float64)
+    dw2_g = dW2.cpu().numpy().astype(np.float64)
+    s_g = O.delayed_scale(amax_prev, 2.0)
+    assert f32_bits(blk.scale_used.item()) == f32_bits(s_g)
+    assert f32_bits(blk.amax_last.item()) == f32_bits(_max_bf16_nonneg(post_g))
+    W2t, _, inv_sw, _ = O.cast_transpose(ins["W2"])
+    assert (W2t == blk.W2t_q.cpu().numpy()).all()
+
+    CH = 4096
+    chunks = [(r0, min(M, r0 + CH)) for r0 in range(0, M, CH)]
+    workers = max(1, min(4, (os.cpu_count() or 4) // 4))
+
+    # pass 1: the oracle's own post, and its amax (the bootstrap amax_prev)
+    def pass1(c):
+        r0, r1 = c
+        return F.bf16_round(O.up_relu2(ins["X"][r0:r1], ins["W1"]))
+
+    with ThreadPoolExecutor(workers) as ex:
+        post_o = np.concatenate(list(ex.map(pass1, chunks)))
+    amax_o = O.amax(F.bf16_to_f64(post_o))
+
+    # pass 2: the rest of both chains, chunk by chunk
+    def pass2(c):
+        r0, r1 = c
+        Xc, dYc = ins["X"][r0:r1], ins["dY"][r0:r1]
+        pg = F.bf16_to_f64(post_g[r0:r1])
+        out = {}
+        # independent chain
+        fo = O.mlp_fwd(Xc, ins["W1"], W2t, inv_sw, amax_o, 2.0, post_bits=post_o[r0:r1])
+        bo = O.mlp_bwd(dYc, Xc, ins["W1"], ins["W2"], F.bf16_to_f64(post_o[r0:r1]))
+        out["post"] = (F.bf16_to_f64(post_g[r0:r1]), F.bf16_to_f64(post_o[r0:r1]))
+        out["y"] = (F.bf16_to_f64(y_g[r0:r1]), F.bf16_to_f64(fo["y"]))
+        out["dx"] = (F.bf16_to_f64(dx_g[r0:r1]), bo["dX"])
+        out["dpre_o"] = (F.bf16_to_f64(dpre_g[r0:r1]), bo["dpre"])
+        out["dw1_o"], out["dw2_o"] = bo["dW1"], bo["dW2"]
+        # given the GPU's intermediates
+        out["codes_ok"] = bool((O.quantize(pg, s_g) == pq_g[r0:r1]).all())
+        out["y_g"] = (out["y"][0], O.down_fp8(pq_g[r0:r1], W2t, O.inv_scale(s_g), inv_sw))
+        bg = O.mlp_bwd(dYc, Xc, ins["W1"], ins["W2"], pg)
+        out["dpre_g"] = (out["dpre_o"][0], bg["dpre"])
+        out["dx_g"] = (out["dx"][0], bg["dX"])
+        out["dw1_g"], out["dw2_g"] = bg["dW1"], bg["dW2"]
+        # partial amax of the tile rows in this chunk (chunks hold whole tile rows)
+        out["tiles"] = (r0 // BM, O.tile_amax(pg, BM, BN))
+        return out
+
+    fro = {k: _Fro() for k in ("post", "y", "dx", "dpre_o", "y_g", "dpre_g", "dx_g")}
+    dw1_o, dw2_o = np.zeros((h, d)), np.zeros((d, h))
+    dw1_gf, dw2_gf = np.zeros((h, d)), np.zeros((d, h))
+    tiles_ok = True
+    with ThreadPoolExecutor(workers) as ex:
+        for out in ex.map(pass2, chunks):
+            assert out["codes_ok"], "post_q codes"
+            for k in fro:
+                fro[k].add(*out[k])
+            dw1_o += out["dw1_o"]
+            dw2_o += out["dw2_o"]
+            dw1_gf += out["dw1_g"]
+            dw2_gf += out["dw2_g"]
+            t0, ta = out["tiles"]
+            tiles_ok &= bool((f32_bits(ta) == f32_bits(part_g[t0:t0 + ta.shape[0]])).all())
+    assert tiles_ok, "partial-amax workspace"
+    # the oracle on its own
+    assert fro["post"].value() < 1e-2, fro["post"].value()
+    assert fro["y"].value() < 2e-2, fro["y"].value()
+    assert fro["dx"].value() < 1e-2, fro["dx"].value()
+    assert fro["dpre_o"].value() < 1e-2, fro["dpre_o"].value()
+    assert rel_fro(dw1_g, dw1_o) < 1e-2
+    assert rel_fro(dw2_g, dw2_o) < 1e-2
+    # fed the GPU's intermediates
+    assert fro["y_g"].value() < 4e-3, fro["y_g"].value()
+    assert fro["dpre_g"].value() < 4e-3, fro["dpre_g"].value()
+    assert fro["dx_g"].value() < 4e-3, fro["dx_g"].value()
+    assert rel_fro(dw1_g, dw1_gf) < 4e-3
+    assert rel_fro(dw2_g, dw2_gf) < 1e-4
 
 
 def test_fwd_two_steps_full_size(fm):

@@ -5,9 +5,13 @@ Gates (element by element on the same seeded inputs):
     and the same amax_prev;
   * amax_out bit-exact against the maximum of the GPU's own post;
   * scale_out bit-exact against the delayed-scale formula;
-  * relative Frobenius error <= 2e-2 for outputs downstream of an e4m3 GEMM
-    (Y in TRAIN) and <= 1e-2 for bf16-path outputs (post, eval Y, dX, dW1,
-    dW2), against the oracle run on its own from the same inputs;
+  * relative Frobenius error <= 2e-2 for Y in TRAIN (downstream of an e4m3
+    GEMM) and <= 1e-2 for post and eval Y, against the oracle's forward run
+    on its own from the same inputs;
+  * the backward (dX, dW1, dW2) against the oracle's backward fed the GPU's
+    bf16 post (the gates 1e-2 and the tighter 4e-3 / 1e-4 below); the
+    oracle's whole chain run on its own is compared at the timed workload's
+    size in test_gpu_fullsize.py;
   * tighter, derived bounds where the oracle is fed the GPU's intermediate
     tensors: Y from the GPU's post_q within the bf16 output rounding
     (2^-8 per element => Frobenius < 4e-3), dX/dW from the GPU's post

@@ -41,6 +41,29 @@ def test_delayed_scale_is_correctly_rounded_fp32():
         assert err <= abs(Fraction(float(lo)) - q) and err <= abs(Fraction(float(hi)) - q)
 
 
+def test_inv_scale_is_correctly_rounded_fp32_reciprocal():
+    """inv_scale(s) is the fp32 value nearest to the exact rational 1/s (ties
+    to the even significand), for scales that are not powers of two as well:
+    checked with exact Fractions against both fp32 neighbours."""
+    g = np.random.default_rng(5)
+    scales = np.float32(np.abs(g.standard_normal(400)) * 10.0 ** g.integers(-8, 8, 400))
+    scales = np.concatenate([scales, np.float32([448.0 / 3.0, 448.0 / 14.0, 0.37, 3.0, 7.0, 2.0 ** -5, 1.0])])
+    for s in scales:
+        inv = O.inv_scale(float(s))
+        assert float(np.float32(inv)) == inv                     # an fp32 value
+        q = 1 / Fraction(float(s))
+        lo = np.nextafter(np.float32(inv), np.float32(0))
+        hi = np.nextafter(np.float32(inv), np.float32(np.inf))
+        err = abs(Fraction(inv) - q)
+        e_lo, e_hi = abs(Fraction(float(lo)) - q), abs(Fraction(float(hi)) - q)
+        assert err <= e_lo and err <= e_hi, s
+        if err in (e_lo, e_hi):                                  # a tie: the even significand wins
+            assert int(np.float32(inv).view(np.uint32)) % 2 == 0
+    # powers of two invert exactly
+    for e in range(-20, 21):
+        assert O.inv_scale(2.0 ** e) == 2.0 ** -e
+
+
 def test_amax_definition():
     x = np.array([[0.5, -3.0], [2.0, 1.0]])
     assert O.amax(x) == 3.0
