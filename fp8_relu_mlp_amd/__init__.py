@@ -351,6 +351,41 @@ class Relu2MLP:
                 self.x_amax_prev.fill_(float(x_amax_init))
         self.refresh_caches()
 
+    # the device tensors whose values carry a block from one step to the next
+    _STATE = ("W1", "W2", "W2t_q", "w2_scale", "w2_inv_scale", "w2_amax", "amax_prev", "scale_used",
+              "amax_hist")
+    _STATE_FP8UP = ("W1t_q", "w1_scale", "w1_inv_scale", "w1_amax", "x_amax_prev", "x_scale")
+
+    def state_dict(self):
+        """The block's step-to-step state as CPU tensors (weights, weight
+        caches with their scales, the delayed-scale amaxes and the window
+        position), for a checkpoint; ``load_state_dict`` restores it so that
+        the following steps give the same bits as an uninterrupted run."""
+        names = self._STATE + (self._STATE_FP8UP if self.fp8_up else ())
+        sd = {k: getattr(self, k).detach().cpu().clone() for k in names}
+        sd["hist_pos"] = torch.tensor(self._hist_pos)
+        sd["w2_refreshed"] = torch.tensor(int(self._w2_refreshed))
+        sd["last_is_hist"] = torch.tensor(int(self.amax_window > 1))
+        return sd
+
+    def load_state_dict(self, sd):
+        """Copy a ``state_dict`` into this block's device buffers (same shapes,
+        same options)."""
+        names = self._STATE + (self._STATE_FP8UP if self.fp8_up else ())
+        for k in names:
+            t = getattr(self, k)
+            if tuple(sd[k].shape) != tuple(t.shape) or sd[k].dtype != t.dtype:
+                raise ValueError(f"state {k}: {tuple(sd[k].shape)} {sd[k].dtype} does not fit {tuple(t.shape)} {t.dtype}")
+            t.copy_(sd[k])
+        self._hist_pos = int(sd["hist_pos"])
+        self._w2_refreshed = bool(int(sd["w2_refreshed"]))
+        if self.amax_window > 1:
+            # the amax last measured sits in the slot before the next write
+            p = (self._hist_pos - 1) % self.amax_window
+            self.amax_last_measured = self.amax_hist[p:p + 1]
+        else:
+            self.amax_last_measured = self.amax_prev
+
     def refresh_w2_cache(self, workspace=None, stream=None):
         if self.w2_policy == "exact" or not self._w2_refreshed:
             fp8_cast_transpose_w2(self.W2, self.W2t_q, self.w2_scale, self.w2_inv_scale, self.w2_amax,

@@ -148,16 +148,24 @@ class Relu2Stack:
         self.steps_done += 1
         return self.state
 
+    def state_dict(self):
+        """Checkpoint of the training state: every layer's ``Relu2MLP`` state
+        (weights, weight caches, delayed-scale amaxes) and the step count,
+        as CPU tensors.  Restored into a stack built with the same options,
+        the following steps reproduce an uninterrupted run bit for bit."""
+        sd = {"steps_done": torch.tensor(self.steps_done)}
+        for l, blk in enumerate(self.layers):
+            for k, v in blk.state_dict().items():
+                sd[f"layer{l}.{k}"] = v
+        return sd
+
+    def load_state_dict(self, sd):
+        for l, blk in enumerate(self.layers):
+            pre = f"layer{l}."
+            blk.load_state_dict({k[len(pre):]: v for k, v in sd.items() if k.startswith(pre)})
+        self.steps_done = int(sd["steps_done"])
+
     def saturation_rate(self, l):
         """Share of layer l's e4m3 post codes at the top code (448) in the
         last step (needs telemetry=True)."""
         return float(self.saturated[l].item()) / float(self._M * self.h)
-
-    def clip_fraction(self, l):
-        """Share of layer l's last post values that the e4m3 copy saturated
-        (post * scale > 448); a diagnostic read with PyTorch, not a step of
-        the method (needs keep_post)."""
-        if not self.keep_post:
-            raise ValueError("clip_fraction reads the bf16 post; use telemetry with keep_post=False")
-        s = self.layers[l].scale_used
-        return float((self.post[l].float() * s > 448.0).float().mean().item())

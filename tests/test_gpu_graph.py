@@ -57,8 +57,10 @@ def test_step_captured_in_a_graph_replays_like_eager():
 
     # the state every run starts from: the W2 cache and a measured amax
     fm.fp8_cast_transpose_w2(W2, W2t, w2_scale, w2_inv, w2_amax, workspace=wsc)
-    fm.mlp_relu2_fwd(fm.TRAIN_FP8, X, W1, W2t, w2_inv, None, amax_prev, 2.0, post, post_q, amax_prev, None, Y,
+    # (amax_out may not alias amax_prev: the launch writes one while it reads the other)
+    fm.mlp_relu2_fwd(fm.TRAIN_FP8, X, W1, W2t, w2_inv, None, amax_prev, 2.0, post, post_q, amax_out, None, Y,
                      workspace=wsf)
+    amax_prev.copy_(amax_out)
     torch.cuda.synchronize()
     start = {k: v.clone() for k, v in (("W1", W1), ("W2", W2), ("W2t", W2t), ("w2_inv", w2_inv),
                                        ("amax_prev", amax_prev))}

@@ -227,3 +227,50 @@ def test_stack_full_size(fm):
     for (t, l), c in sorted(rec.caps.items()):
         case(f"stack full size: oracle check layer {l} step {t}")
         check_layer(c, cols, stk.lr_step)
+
+
+@pytest.mark.parametrize("opts", [{}, {"fp8_up": True, "amax_window": 3, "w2_scale": "delayed", "w2_margin": 1.5}])
+def test_stack_checkpoint_resume_bit_identical(fm, opts):
+    """Stop a 3-layer stack after step k, save its state (torch.save to a
+    byte buffer, loaded back with weights_only), load it into a freshly built
+    stack and continue: every weight, cache, amax and output of the following
+    steps equals the uninterrupted run bit for bit."""
+    import io
+    from fp8_relu_mlp_amd.stack import Relu2Stack
+    L, M, d, h, steps, stop = 3, 1536, 256, 768, 5, 2
+    case(f"stack checkpoint/resume L={L} M={M} d={d} h={h} opts={opts}")
+    ws = [synth.mlp_inputs(8, d, h, 100 + l) for l in range(L)]
+    batches = [synth.mlp_inputs(M, d, h, 200 + t, with_dy=True) for t in range(steps)]
+
+    def fresh():
+        return Relu2Stack([bf16_dev(w["W1"]) for w in ws], [bf16_dev(w["W2"]) for w in ws], margin=MARGIN,
+                          lr=1e-3, **opts)
+
+    def snapshot(st):
+        torch.cuda.synchronize()
+        return {k: v.reshape(-1).contiguous().view(torch.uint8).numpy().copy() for k, v in st.state_dict().items()}
+
+    def run(st, t0, t1):
+        outs = []
+        for t in range(t0, t1):
+            state = st.step(bf16_dev(batches[t]["X"]), bf16_dev(batches[t]["dY"]))
+            torch.cuda.synchronize()
+            outs.append((state.cpu().numpy().copy(), bits(st.x[L]), snapshot(st)))
+        return outs
+
+    full = run(fresh(), 0, steps)
+    a = fresh()
+    run(a, 0, stop)
+    buf = io.BytesIO()
+    torch.save(a.state_dict(), buf)
+    del a
+    buf.seek(0)
+    b = fresh()
+    b.load_state_dict(torch.load(buf, weights_only=True))
+    resumed = run(b, stop, steps)
+    for (s_full, x_full, sd_full), (s_res, x_res, sd_res) in zip(full[stop:], resumed):
+        assert (f32_bits(s_full) == f32_bits(s_res)).all()
+        assert (x_full == x_res).all()
+        assert sd_full.keys() == sd_res.keys()
+        for k in sd_full:
+            assert sd_full[k].tobytes() == sd_res[k].tobytes(), k
