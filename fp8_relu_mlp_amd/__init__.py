@@ -7,7 +7,7 @@ PyTorch supplies device memory and streams and nothing else.  If the library
 is not built, the first call raises.
 
 Entry points (same names as the C ABI):
-  mlp_relu2_fwd, mlp_relu2_fwd_fp8up, mlp_relu2_bwd, mlp_relu2_bwd_fp8post, fp8_cast_transpose, fp8_cast_transpose_w2,
+  mlp_relu2_fwd, mlp_relu2_fwd_noalloc, mlp_relu2_fwd_fp8up, mlp_relu2_bwd, mlp_relu2_bwd_fp8post, fp8_cast_transpose, fp8_cast_transpose_w2,
   amax_reduce, fp8_scale_from_amax, fp8_linear, fp8_saturation_count,
   softcap_ce_fwd_bwd, softcap_ce_fwd_bwd_fp8, and the layer-stack helpers
   rmsnorm_fwd, rmsnorm_bwd, add_bf16, sgd_update_bf16
@@ -24,7 +24,7 @@ EVAL_BF16 = 1
 F32 = 0
 BF16 = 1
 
-__all__ = ["mlp_relu2_fwd", "mlp_relu2_fwd_fp8up", "mlp_relu2_bwd", "mlp_relu2_bwd_fp8post", "fp8_cast_transpose", "fp8_cast_transpose_w2", "amax_reduce",
+__all__ = ["mlp_relu2_fwd", "mlp_relu2_fwd_noalloc", "mlp_relu2_fwd_fp8up", "mlp_relu2_bwd", "mlp_relu2_bwd_fp8post", "fp8_cast_transpose", "fp8_cast_transpose_w2", "amax_reduce",
            "fp8_scale_from_amax", "fp8_linear", "fp8_saturation_count", "softcap_ce_fwd_bwd", "softcap_ce_fwd_bwd_fp8",
            "rmsnorm_fwd", "rmsnorm_bwd", "add_bf16", "sgd_update_bf16",
            "Relu2MLP", "KernelTimer", "Fp8MlpError", "TRAIN_FP8", "EVAL_BF16"]
@@ -66,6 +66,17 @@ def mlp_relu2_fwd(mode, X, W1, W2t_q, w2_inv_scale, W2, amax_prev, margin, post,
     check("mlp_relu2_fwd", L.mlp_relu2_fwd(
         mode, _p(X), _p(W1), _p(W2t_q), _p(w2_inv_scale), _p(W2), _p(amax_prev), float(margin), _p(post),
         _p(post_q), _p(amax_out), _p(scale_out), _p(Y), M, d, h, _p(ws), wsb, _stream(stream)))
+
+
+def mlp_relu2_fwd_noalloc(mode, X, W1, W2t_q, w2_inv_scale, W2, amax_prev, margin, post, post_q, amax_out,
+                          scale_out, Y, stream=None):
+    """See mlp_relu2_fwd_noalloc in include/fp8mlp.h: mlp_relu2_fwd without a
+    workspace (the library's per-GPU scratch array holds the partial amax)."""
+    M, d = X.shape
+    h = W1.shape[0]
+    check("mlp_relu2_fwd_noalloc", lib().mlp_relu2_fwd_noalloc(
+        mode, _p(X), _p(W1), _p(W2t_q), _p(w2_inv_scale), _p(W2), _p(amax_prev), float(margin), _p(post),
+        _p(post_q), _p(amax_out), _p(scale_out), _p(Y), M, d, h, _stream(stream)))
 
 
 def mlp_relu2_fwd_fp8up(X, x_scale, W1t_q, w1_inv_scale, W2t_q, w2_inv_scale, amax_prev, margin, post, post_q,

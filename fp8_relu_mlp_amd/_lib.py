@@ -26,6 +26,9 @@ SIGNATURES = {
     "mlp_relu2_fwd_workspace": (c_size, [c_i64, c_i64, c_i64]),
     "mlp_relu2_fwd": (c_int, [c_int, vp, vp, vp, vp, vp, vp, c_float, vp, vp, vp, vp, vp,
                               c_i64, c_i64, c_i64, vp, c_size, vp]),
+    "mlp_relu2_fwd_noalloc_max_bytes": (c_size, []),
+    "mlp_relu2_fwd_noalloc": (c_int, [c_int, vp, vp, vp, vp, vp, vp, c_float, vp, vp, vp, vp, vp,
+                                      c_i64, c_i64, c_i64, vp]),
     "mlp_relu2_fwd_fp8up_workspace": (c_size, [c_i64, c_i64, c_i64]),
     "mlp_relu2_fwd_fp8up": (c_int, [vp, vp, vp, vp, vp, vp, vp, c_float, vp, vp, vp, vp, vp, vp,
                                     c_i64, c_i64, c_i64, vp, c_size, vp]),

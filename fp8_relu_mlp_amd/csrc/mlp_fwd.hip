@@ -1,6 +1,9 @@
 // mlp_relu2_fwd: fused up-projection + ReLU^2 + e4m3 quantisation + partial
 // amax, the partial-amax reduction, and the FP8 (or, at eval, bf16)
 // down-projection.  All launches go to the caller's stream, back to back.
+#include <atomic>
+#include <mutex>
+
 #include "launch.h"
 
 namespace fp8mlp {
@@ -34,21 +37,11 @@ static FwdPlan fwd_plan(int64_t M, int64_t h) {
   return p;
 }
 
-}  // namespace fp8mlp
-
-using namespace fp8mlp;
-
-extern "C" {
-
-size_t mlp_relu2_fwd_workspace(int64_t M, int64_t d, int64_t h) {
-  if (M < 0 || d <= 0 || h <= 0) return 0;
-  return fwd_plan(M, h).partial_bytes;
-}
-
-int mlp_relu2_fwd(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t* W2t_q,
-                  const float* w2_inv_scale, const uint16_t* W2, const float* amax_prev, float margin,
-                  uint16_t* post, uint8_t* post_q, float* amax_out, float* scale_out, uint16_t* Y, int64_t M,
-                  int64_t d, int64_t h, void* workspace, size_t workspace_bytes, void* stream) {
+// Argument checks of mlp_relu2_fwd that do not involve the workspace.
+static int fwd_check_args(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t* W2t_q,
+                          const float* w2_inv_scale, const uint16_t* W2, const float* amax_prev, float margin,
+                          const uint16_t* post, const uint8_t* post_q, const float* amax_out, const float* scale_out,
+                          const uint16_t* Y, int64_t M, int64_t d, int64_t h) {
   const bool train = mode == FP8MLP_TRAIN_FP8;
   FP8MLP_REQUIRE(mode == FP8MLP_TRAIN_FP8 || mode == FP8MLP_EVAL_BF16, FP8MLP_E_ARG);
   FP8MLP_REQUIRE(M >= 0 && d > 0 && h > 0 && d % 64 == 0 && h % 64 == 0, FP8MLP_E_SHAPE);
@@ -71,14 +64,16 @@ int mlp_relu2_fwd(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t
   for (const void* p : {(const void*)w2_inv_scale, (const void*)amax_prev, (const void*)amax_out,
                         (const void*)scale_out})
     FP8MLP_REQUIRE(((uintptr_t)p & 3) == 0, FP8MLP_E_ALIGN);
-  const FwdPlan plan = fwd_plan(M, h);
-  FP8MLP_REQUIRE(workspace_bytes >= plan.partial_bytes && (plan.partial_bytes == 0 || workspace),
-                 FP8MLP_E_WORKSPACE);
-  FP8MLP_REQUIRE(plan.partial_bytes == 0 || aligned16(workspace), FP8MLP_E_ALIGN);
-  FP8MLP_TRY(check_device());
+  return FP8MLP_OK;
+}
 
-  hipStream_t st = (hipStream_t)stream;
-  float* partial = (float*)workspace;
+// The launches of mlp_relu2_fwd; `partial` holds fwd_plan(M, h).partial_bytes.
+static int fwd_launch(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t* W2t_q,
+                      const float* w2_inv_scale, const uint16_t* W2, const float* amax_prev, float margin,
+                      uint16_t* post, uint8_t* post_q, float* amax_out, float* scale_out, uint16_t* Y, int64_t M,
+                      int64_t d, int64_t h, float* partial, hipStream_t st) {
+  const bool train = mode == FP8MLP_TRAIN_FP8;
+  const FwdPlan plan = fwd_plan(M, h);
 
   // 1. up-projection with the fused ReLU^2 / quantise / partial-amax epilogue
   {
@@ -112,6 +107,83 @@ int mlp_relu2_fwd(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t
     FP8MLP_TRY(launch_gemm<CfgDownBf16, KID_DOWN_BF16>(a, epi, st));
   }
   return FP8MLP_OK;
+}
+
+// ------------------------------------------------------------------ allocation-free forward
+// The partial-amax tensor of mlp_relu2_fwd_noalloc lives in this file-scope
+// device array instead of a caller workspace: one copy per GPU, held until the
+// process ends, shared by every call on that GPU.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol);
+// it passes the device address that hipGetSymbolAddress returns, looked up
+// once per device on the first call with that device current.
+constexpr size_t kFwdScratchBytes = 256 * 1024;
+static __device__ __align__(256) uint8_t scratch[kFwdScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+// Device address of this GPU's scratch array.
+static int scratch_ptr(void** out) {
+  int dev = 0;
+  FP8MLP_TRY(hip_status(hipGetDevice(&dev)));
+  if (dev < 0 || dev >= kScratchDevices) return FP8MLP_E_ARCH;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      FP8MLP_TRY(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))));
+      if (p == nullptr) return FP8MLP_E_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FP8MLP_OK;
+}
+
+}  // namespace fp8mlp
+
+using namespace fp8mlp;
+
+extern "C" {
+
+size_t mlp_relu2_fwd_workspace(int64_t M, int64_t d, int64_t h) {
+  if (M < 0 || d <= 0 || h <= 0) return 0;
+  return fwd_plan(M, h).partial_bytes;
+}
+
+int mlp_relu2_fwd(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t* W2t_q,
+                  const float* w2_inv_scale, const uint16_t* W2, const float* amax_prev, float margin,
+                  uint16_t* post, uint8_t* post_q, float* amax_out, float* scale_out, uint16_t* Y, int64_t M,
+                  int64_t d, int64_t h, void* workspace, size_t workspace_bytes, void* stream) {
+  FP8MLP_TRY(fwd_check_args(mode, X, W1, W2t_q, w2_inv_scale, W2, amax_prev, margin, post, post_q, amax_out,
+                            scale_out, Y, M, d, h));
+  const FwdPlan plan = fwd_plan(M, h);
+  FP8MLP_REQUIRE(workspace_bytes >= plan.partial_bytes && (plan.partial_bytes == 0 || workspace),
+                 FP8MLP_E_WORKSPACE);
+  FP8MLP_REQUIRE(plan.partial_bytes == 0 || aligned16(workspace), FP8MLP_E_ALIGN);
+  FP8MLP_TRY(check_device());
+  return fwd_launch(mode, X, W1, W2t_q, w2_inv_scale, W2, amax_prev, margin, post, post_q, amax_out, scale_out, Y,
+                    M, d, h, (float*)workspace, (hipStream_t)stream);
+}
+
+size_t mlp_relu2_fwd_noalloc_max_bytes(void) { return kFwdScratchBytes; }
+
+int mlp_relu2_fwd_noalloc(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t* W2t_q,
+                          const float* w2_inv_scale, const uint16_t* W2, const float* amax_prev, float margin,
+                          uint16_t* post, uint8_t* post_q, float* amax_out, float* scale_out, uint16_t* Y, int64_t M,
+                          int64_t d, int64_t h, void* stream) {
+  FP8MLP_TRY(fwd_check_args(mode, X, W1, W2t_q, w2_inv_scale, W2, amax_prev, margin, post, post_q, amax_out,
+                            scale_out, Y, M, d, h));
+  FP8MLP_REQUIRE(fwd_plan(M, h).partial_bytes <= kFwdScratchBytes, FP8MLP_E_WORKSPACE);
+  FP8MLP_TRY(check_device());
+  void* ptr = nullptr;
+  FP8MLP_TRY(scratch_ptr(&ptr));
+  return fwd_launch(mode, X, W1, W2t_q, w2_inv_scale, W2, amax_prev, margin, post, post_q, amax_out, scale_out, Y,
+                    M, d, h, (float*)ptr, (hipStream_t)stream);
 }
 
 size_t mlp_relu2_fwd_fp8up_workspace(int64_t M, int64_t d, int64_t h) {

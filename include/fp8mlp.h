@@ -113,6 +113,28 @@ int mlp_relu2_fwd(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t
                   int64_t M, int64_t d, int64_t h, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * mlp_relu2_fwd_noalloc -- mlp_relu2_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, kernels and
+ * results as mlp_relu2_fwd, with no workspace argument.  The partial-amax
+ * tensor lives in a scratch array inside the library, one per GPU, kept
+ * until the process ends and shared by every call on that GPU; it needs
+ * mlp_relu2_fwd_workspace(M, d, h) bytes, at most
+ * mlp_relu2_fwd_noalloc_max_bytes() (256 KB: M * h up to about 4.3e9 with
+ * 256 x 256 tiles), else FP8MLP_E_WORKSPACE.  Nothing in the scratch array
+ * needs to start at zero (every entry a call reads, the same call writes
+ * first).  The call allocates and frees nothing; its first call on a device
+ * looks up the array's device address once.  Calls that overlap on one GPU
+ * (on different streams, without ordering) race on the array.
+ * Arguments and errors otherwise as mlp_relu2_fwd.
+ * ---------------------------------------------------------------------- */
+size_t mlp_relu2_fwd_noalloc_max_bytes(void);
+int mlp_relu2_fwd_noalloc(int mode, const uint16_t* X, const uint16_t* W1, const uint8_t* W2t_q,
+                          const float* w2_inv_scale, const uint16_t* W2, const float* amax_prev, float margin,
+                          uint16_t* post, uint8_t* post_q, float* amax_out, float* scale_out, uint16_t* Y,
+                          int64_t M, int64_t d, int64_t h, void* stream);
+
+/* ------------------------------------------------------------------------
  * mlp_relu2_bwd -- the bf16 backward of the block, straight through the FP8
  * forward ("A Retrospective on Our World Records", Main Track: the BF16
  * backward path is left unchanged; "NanoGPT Speedrun (Track 1)", "Changes vs

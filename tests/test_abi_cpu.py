@@ -114,6 +114,15 @@ def test_fwd_validation_before_any_device_call(L_nogpu):
     assert _fwd(L, ws=None) == E_WS
     assert _fwd(L, wsb=8) == E_WS
     assert _fwd(L, mode=1, W2=None) == E_NULL   # eval needs the bf16 W2
+    # the allocation-free variant: the same checks, and a size limit instead of a workspace
+    nf = lambda **kw: L.mlp_relu2_fwd_noalloc(*[v for k, v in dict(
+        dict(mode=0, X=16, W1=16, W2t_q=16, w2_inv=16, W2=None, amax_prev=32, margin=2.0, post=16, post_q=16,
+             amax_out=48, scale_out=None, Y=16, M=256, d=128, h=512, stream=None), **kw).items()])
+    assert L.mlp_relu2_fwd_noalloc_max_bytes() == 256 * 1024
+    assert nf(d=100) == E_SHAPE
+    assert nf(X=None) == E_NULL
+    assert nf(amax_out=32) == E_ARG
+    assert nf(M=1 << 20, h=1 << 15) == E_WS                    # partial amax > 256 KB
     # amax_t is written while amax_{t-1} is still read: no aliasing
     assert _fwd(L, amax_out=32) == E_ARG
     assert _fwd(L, scale_out=32) == E_ARG
