@@ -436,6 +436,55 @@ struct EpiDpreQ {
   }
 };
 
+// One split-k partial of a weight gradient, written in the order the
+// accumulators sit in the registers rather than row-major: position
+// ((((fm * FN + fn) * 4 + j) * NW + wave) * 64 + lane) of the tile's
+// BM * BN floats holds elements 4j .. 4j+3 of fragment (fm, fn) of that lane,
+// so every store instruction of a wave writes 1 KB contiguously (row-major
+// stores from the accumulator layout would touch 32 rows per instruction).
+// The partials are internal: k_splitk_reduce_tiles, which sums them, maps the
+// positions back to rows and columns.  Tile (tm, tn) of split s starts at
+// part + s * split_stride + (tm * tiles_n + tn) * BM * BN.  With div_by, every
+// value is first multiplied by fp32(1 / *div_by).
+struct EpiF32Part {
+  float* part;
+  int64_t split_stride;   // floats between the partials of consecutive splits
+  int tiles_n;
+  const float* div_by = nullptr;
+
+  template <class C>
+  static constexpr int lds_bytes() { return 0; }
+
+  template <class C>
+  __device__ __forceinline__ void run(const TileCtx& c, f32x16 (&acc)[C::FM][C::FN], FP8MLP_LDS char*) {
+    const int wave = threadIdx.x >> 6;
+    float* base = part + (int64_t)c.split * split_stride + (int64_t)(c.tm * tiles_n + c.tn) * (C::BM * C::BN);
+    const float f = div_by ? 1.0f / *div_by : 1.0f;
+    auto stores = [&]<bool DIV>() {
+#pragma unroll
+      for (int fm = 0; fm < C::FM; fm++)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; fn++)
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            float4 v = {acc[fm][fn][4 * j], acc[fm][fn][4 * j + 1], acc[fm][fn][4 * j + 2], acc[fm][fn][4 * j + 3]};
+            if constexpr (DIV) {
+              v.x *= f;
+              v.y *= f;
+              v.z *= f;
+              v.w *= f;
+            }
+            *(float4*)(base + ((((fm * C::FN + fn) * 4 + j) * C::NW + wave) * 64 + c.lane) * 4) = v;
+          }
+    };
+    if (div_by) {
+      stores.template operator()<true>();
+    } else {
+      stores.template operator()<false>();
+    }
+  }
+};
+
 // fp32 output: either the final weight gradient (optionally added to what is
 // there) or one split-k partial, written to out + split * split_stride.  With
 // div_by, every value is first multiplied by fp32(1 / *div_by) (the e4m3

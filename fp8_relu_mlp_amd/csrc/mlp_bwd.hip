@@ -30,6 +30,7 @@ struct BwdPlan {
   size_t dpre_bytes, wt_bytes, part_bytes;   // dpre; W1t + W2t; split-k partials of dW1 and dW2
   int splits;
   int64_t k_per_split;
+  int64_t split_stride;                      // floats per split partial (whole tiles of one gradient)
 };
 
 static BwdPlan bwd_plan(int64_t M, int64_t d, int64_t h) {
@@ -45,8 +46,11 @@ static BwdPlan bwd_plan(int64_t M, int64_t d, int64_t h) {
   p.k_per_split = cdiv(cdiv(M, s), 64) * 64;
   if (p.k_per_split == 0) p.k_per_split = 64;
   p.splits = (int)(M > 0 ? cdiv(M, p.k_per_split) : 1);
-  // the partials of dW1, then those of dW2
-  p.part_bytes = p.splits > 1 ? 2 * align_up((size_t)p.splits * (size_t)(h * d) * 4, 256) : 0;
+  // the partials of dW1, then those of dW2, each split a whole number of
+  // tiles (dW1 [h, d] and dW2 [d, h] have the same tile count)
+  static_assert(CfgDw::BM == CfgDw::BN, "dW1 and dW2 tile the same way");
+  p.split_stride = tiles * CfgDw::BM * CfgDw::BN;
+  p.part_bytes = p.splits > 1 ? 2 * align_up((size_t)p.splits * (size_t)p.split_stride * 4, 256) : 0;
   return p;
 }
 
@@ -124,33 +128,85 @@ __global__ void __launch_bounds__(256) k_fill_zero(float4* __restrict__ out, int
     out[i] = float4{0.f, 0.f, 0.f, 0.f};
 }
 
-// Two reductions of the same shape in one launch (blockIdx.y picks the pair).
-__global__ void __launch_bounds__(256) k_splitk_reduce2(const float4* __restrict__ part0, float4* __restrict__ out0,
-                                                        const float4* __restrict__ part1, float4* __restrict__ out1,
-                                                        int splits, int64_t n4, int accumulate) {
-  const float4* part = blockIdx.y ? part1 : part0;
-  float4* out = blockIdx.y ? out1 : out0;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
-    float4 a = accumulate ? out[i] : float4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < splits; s++) {
-      const float4 v = part[s * n4 + i];
-      a.x += v.x;
-      a.y += v.y;
-      a.z += v.z;
-      a.w += v.w;
+// One weight gradient whose split-k partials EpiF32Part wrote.
+struct RedProb {
+  const float* part;     // split s at part + s * split_stride
+  float* out;            // [rows, cols] fp32, leading dimension cols
+  int64_t rows, cols;
+  int tiles_n, tiles;
+  int perm;              // 1: a lane holds 16 consecutive columns of a fragment (GemmCfg::PERM)
+};
+
+// out = (accumulate ? out : 0) + part[0] + part[1] + ... in split order, for
+// the partials EpiF32Part wrote with the tile configuration C.  Block
+// (g, t, z): problem z, tile t, the 32 rows of fragment row g (the wave row
+// wm = g / FM, fragment fm = g % FM); it sums the partials of those rows
+// (contiguous 16-byte reads), stages the 32 x BN result in LDS and writes it
+// row by row.
+template <class C>
+__global__ void __launch_bounds__(256) k_splitk_reduce_tiles(RedProb p0, RedProb p1, int splits,
+                                                             int64_t split_stride, int accumulate) {
+  static_assert(C::NW == 8 && C::BN % 64 == 0 && (32 * C::BN / 4) % 256 == 0, "two-group tiles");
+  constexpr int C4 = C::BN / 4;                     // float4 per tile row
+  constexpr int PER = 32 * C4 / 256;                // float4 per thread
+  __shared__ float4 img[32][C4 + 1];
+  const RedProb& P = blockIdx.z ? p1 : p0;
+  const int tile = blockIdx.y;
+  if (tile >= P.tiles) return;
+  const int tm = tile / P.tiles_n, tn = tile % P.tiles_n;
+  const int wm = blockIdx.x / C::FM, fm = blockIdx.x % C::FM;
+  const int64_t m0 = (int64_t)tm * C::BM + wm * C::WTM + fm * 32, n0 = (int64_t)tn * C::BN;
+  const float* base = P.part + (int64_t)tile * (C::BM * C::BN);
+  int pos[PER], rr[PER], cc[PER];
+  float4 a[PER];
+#pragma unroll
+  for (int k = 0; k < PER; k++) {
+    const int i = threadIdx.x + 256 * k;
+    const int b = i >> 6, lane = i & 63;
+    // the four waves of wave row wm, then fragment column fn, then float4 j
+    const int wi = b / (4 * C::FN), fn = (b >> 2) % C::FN, j = b & 3;
+    const int w = (wi & 1) + 2 * wm + 4 * (wi >> 1);
+    const int wn = 2 * (w & 1) + (w >> 2);
+    pos[k] = (((fm * C::FN + fn) * 4 + j) * C::NW + w) * 64 + lane;
+    const int h = lane >> 5;
+    rr[k] = lane & 31;
+    cc[k] = wn * C::WTN + fn * 32 + (P.perm ? 16 * h + 4 * j : 8 * j + 4 * h);
+    a[k] = float4{0.f, 0.f, 0.f, 0.f};
+    if (accumulate && m0 + rr[k] < P.rows && n0 + cc[k] < P.cols)
+      a[k] = *(const float4*)(P.out + (m0 + rr[k]) * P.cols + n0 + cc[k]);
+  }
+  // every split's loads in flight together, then added in split order
+  for (int s = 0; s < splits; s++) {
+    f32x4 v[PER];
+#pragma unroll
+    for (int k = 0; k < PER; k++) v[k] = __builtin_nontemporal_load((const f32x4*)(base + s * split_stride) + pos[k]);
+#pragma unroll
+    for (int k = 0; k < PER; k++) {
+      a[k].x += v[k][0];
+      a[k].y += v[k][1];
+      a[k].z += v[k][2];
+      a[k].w += v[k][3];
     }
-    out[i] = a;
+  }
+#pragma unroll
+  for (int k = 0; k < PER; k++) img[rr[k]][cc[k] >> 2] = a[k];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < PER; k++) {
+    const int i = threadIdx.x + 256 * k;
+    const int r = i / C4, c4 = i % C4;
+    const int64_t m = m0 + r, n = n0 + 4 * c4;
+    if (m < P.rows && n < P.cols) *(float4*)(P.out + m * P.cols + n) = img[r][c4];
   }
 }
 
-static int launch_reduce2(const float* part0, float* out0, const float* part1, float* out1, int splits, int64_t n,
-                          int accumulate, hipStream_t st) {
-  const int64_t n4 = n / 4;
-  int64_t blocks = cdiv(n4, 256);
-  if (blocks > 2048) blocks = 2048;
+template <class C>
+static int launch_reduce_tiles(const RedProb& p0, const RedProb& p1, int splits, int64_t split_stride,
+                               int accumulate, hipStream_t st) {
+  const int tiles = p0.tiles > p1.tiles ? p0.tiles : p1.tiles;
   TraceScope trace("splitk_reduce", st);
-  hipLaunchKernelGGL(k_splitk_reduce2, dim3((unsigned)blocks, 2), dim3(256), 0, st, (const float4*)part0,
-                     (float4*)out0, (const float4*)part1, (float4*)out1, splits, n4, accumulate);
+  hipLaunchKernelGGL(k_splitk_reduce_tiles<C>, dim3(2 * C::FM, (unsigned)tiles, 2), dim3(256), 0, st, p0, p1,
+                     splits, split_stride, accumulate);
   return launch_status();
 }
 
@@ -234,18 +290,34 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* W
     GemmArgs a2{dY, d, post, h, d, h, M, (int)cdiv(d, CfgDw::BM), (int)cdiv(h, CfgDw::BN), plan.splits,
                 plan.k_per_split};
     const bool split = plan.splits > 1;
-    float* part2 = part + (size_t)plan.splits * (size_t)(h * d);
+    float* part2 = part + (size_t)plan.splits * (size_t)plan.split_stride;
     const float* div2 = Q ? post_scale : nullptr;
-    const EpiF32 e1 = split ? EpiF32{part, d, h * d, 0, nullptr} : EpiF32{dW1, d, 0, accumulate, nullptr};
-    const EpiF32 e2 = split ? EpiF32{part2, h, d * h, 0, div2} : EpiF32{dW2, h, 0, accumulate, div2};
-    if constexpr (Q) {
-      FP8MLP_TRY((launch_gemm<CfgDw, KID_DW1>(a1, e1, st)));
-      FP8MLP_TRY((launch_gemm<CfgDw2q, KID_DW2>(a2, e2, st)));
+    if (split) {
+      static_assert(CfgDw2q::FM == CfgDw::FM && CfgDw2q::FN == CfgDw::FN && CfgDw2q::NW == CfgDw::NW &&
+                        CfgDw2q::WTM == CfgDw::WTM && CfgDw2q::WTN == CfgDw::WTN,
+                    "one partial layout for both gradients");
+      const EpiF32Part e1{part, plan.split_stride, a1.tiles_n, nullptr};
+      const EpiF32Part e2{part2, plan.split_stride, a2.tiles_n, div2};
+      if constexpr (Q) {
+        FP8MLP_TRY((launch_gemm<CfgDw, KID_DW1>(a1, e1, st)));
+        FP8MLP_TRY((launch_gemm<CfgDw2q, KID_DW2>(a2, e2, st)));
+      } else {
+        // both in one launch (same tiles, same kernel)
+        FP8MLP_TRY((launch_gemm2<CfgDw, KID_DW>(a1, e1, a2, e2, st)));
+      }
+      const RedProb r1{part, dW1, h, d, a1.tiles_n, a1.tiles_m * a1.tiles_n, CfgDw::PERM ? 1 : 0};
+      const RedProb r2{part2, dW2, d, h, a2.tiles_n, a2.tiles_m * a2.tiles_n, (Q ? CfgDw2q::PERM : CfgDw::PERM) ? 1 : 0};
+      FP8MLP_TRY(launch_reduce_tiles<CfgDw>(r1, r2, plan.splits, plan.split_stride, accumulate, st));
     } else {
-      // both in one launch (same tiles, same kernel)
-      FP8MLP_TRY((launch_gemm2<CfgDw, KID_DW>(a1, e1, a2, e2, st)));
+      const EpiF32 e1{dW1, d, 0, accumulate, nullptr};
+      const EpiF32 e2{dW2, h, 0, accumulate, div2};
+      if constexpr (Q) {
+        FP8MLP_TRY((launch_gemm<CfgDw, KID_DW1>(a1, e1, st)));
+        FP8MLP_TRY((launch_gemm<CfgDw2q, KID_DW2>(a2, e2, st)));
+      } else {
+        FP8MLP_TRY((launch_gemm2<CfgDw, KID_DW>(a1, e1, a2, e2, st)));
+      }
     }
-    if (split) FP8MLP_TRY(launch_reduce2(part, dW1, part2, dW2, plan.splits, h * d, accumulate, st));
   }
   return FP8MLP_OK;
 }
