@@ -32,6 +32,21 @@ int check_device() {
   return st == 1 ? FP8MLP_OK : FP8MLP_E_ARCH;
 }
 
+namespace {
+std::atomic<int> g_dev_cus[kMaxDevices];
+}  // namespace
+
+int num_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = g_dev_cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_dev_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // ------------------------------------------------------------------ amax
 // Maximum of |x| taken on bit patterns: for fp32, |x| bits order like the
 // values (+0 < ... < +inf < NaN), so the unsigned maximum is exact, NaN

@@ -163,10 +163,17 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 __device__ __forceinline__ i32x4 lds_read_b128(const FP8MLP_LDS char* base, uint32_t off) {
   return *(const FP8MLP_LDS i32x4*)(base + off);
 }
-__device__ __forceinline__ i16x4 lds_read_tr16(const FP8MLP_LDS char* base, uint32_t off) {
+// The transposing reads.  Their base is declared __restrict__ so that the
+// read carries alias information: an LDS read without it makes the compiler
+// wait for every buffer_load ... lds still in flight (vmcnt(0)) before it, in
+// case that load writes the bytes read, which in the GEMM main loops would
+// cut the prefetch distance of every k-tile to one phase.  Those loops order
+// their LDS reads after the loads they need with explicit vmcnt waits and
+// block barriers.
+__device__ __forceinline__ i16x4 lds_read_tr16(const FP8MLP_LDS char* __restrict__ base, uint32_t off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FP8MLP_LDS i16x4*)(base + off));
 }
-__device__ __forceinline__ i32x2 lds_read_tr8(const FP8MLP_LDS char* base, uint32_t off) {
+__device__ __forceinline__ i32x2 lds_read_tr8(const FP8MLP_LDS char* __restrict__ base, uint32_t off) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((FP8MLP_LDS i32x2*)(base + off));
 }
 

@@ -16,6 +16,8 @@ extern thread_local int g_last_hip_error;
 // FP8MLP_OK when the current device is gfx950, FP8MLP_E_ARCH otherwise,
 // FP8MLP_E_HIP if the device cannot be queried.  Cached per device.
 int check_device();
+// Compute units of the current device (256 on MI355X; cached per device).
+int num_cus();
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 

@@ -10,7 +10,7 @@
 // W1 and W2 are first transposed into the workspace (4.7 MB each at the
 // GPT-2-small shape) so that both dgrad GEMMs read k-contiguous operands
 // with plain 16-byte LDS reads.
-#include "launch.h"
+#include "persist.h"
 
 namespace fp8mlp {
 
@@ -271,7 +271,8 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* W
       FP8MLP_TRY(launch_gemm<CfgDpost, KID_DPOST>(a, epi, st));
     } else {
       EpiDpre epi{(const uint16_t*)post, dpre, h};
-      FP8MLP_TRY(launch_gemm<CfgDpost, KID_DPOST>(a, epi, st));
+      EpiDpreWP wp{(const uint16_t*)post, dpre, h};
+      FP8MLP_TRY((launch_gemm_persist<CfgDpost, KID_DPOST>(a, wp, epi, st)));
     }
   }
   // 2. dX = dpre W1
