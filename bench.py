@@ -445,6 +445,28 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic.get(dom),
                 "algorithmic_flops_per_launch": fl, "algorithmic_bytes_per_launch": by}
 
+    # the same step replayed from a HIP graph (two steps per graph, so the
+    # forward's amax buffer swap comes back to the captured roles); no entry
+    # point allocates, synchronises or reads a device value, so capture holds
+    log("graph replay pass")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+        step()
+    torch.cuda.synchronize()
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // 2)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / (2 * reps)
+    del graph
+    log(f"graph replay: {graph_ms:.3f} ms/step")
+
     # matrix-core rate on the workload's own operands (the clock under a dense
     # MFMA load depends on the data; the published peaks assume 2.4 GHz)
     log("matrix-core rate probe")
@@ -484,6 +506,9 @@ def main():
         "config": {"workload": "relu2_mlp_fwd_bwd_gpt2_small", "M": M, "d": D, "h": H, "margin": MARGIN,
                    "step": "fwd(train)+bwd+W2 cache refresh"},
         "pct_mixed_mfma_peak": round(100.0 * floor_us / (ms * 1e3), 2),
+        "graph_replay": {"ms_per_step": round(graph_ms, 4), "value": round(flops / (graph_ms * 1e-3) / 1e12, 2),
+                         "pct_mixed_mfma_peak": round(100.0 * floor_us / (graph_ms * 1e3), 2),
+                         "steps": 2 * reps, "how": "fwd+bwd+W2 refresh, two steps per captured HIP graph"},
         "mixed_mfma_floor_us": round(floor_us, 1),
         "roofline": roofline,
         "mfma_probe": probe,
