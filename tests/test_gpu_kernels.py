@@ -96,7 +96,7 @@ def test_cast_transpose_all_bf16_patterns(fm, scale):
     assert f32_bits(inv_out.item()) == f32_bits(rinv)
 
 
-@pytest.mark.parametrize("shape", [(768, 3072), (3072, 768), (2304, 768), (48, 80)])
+@pytest.mark.parametrize("shape", [(768, 3072), (3072, 768), (2304, 768), (48, 80), (1040, 784), (2064, 4096)])
 def test_cast_transpose_exact_scale(fm, shape):
     N, K = shape
     case(f"fp8_cast_transpose exact N={N} K={K}")
