@@ -43,7 +43,7 @@ KID_NAMES = {1: "up_gemm_relu2_quant", 2: "down_gemm_e4m3", 3: "down_gemm_bf16_e
              10: "ce_head_gemm_stats", 11: "ce_head_gemm_grad", 12: "ce_dx_gemm", 13: "ce_dw_gemm",
              14: "ce_head_gemm_e4m3_stats", 15: "ce_head_gemm_e4m3_grad", 16: "dw_gemm"}
 OTHER_NAMES = {"k_max_final": "amax_final", "k_amax_partial": "amax_partial", "k_cast_transpose": "cast_transpose",
-               "k_splitk_reduce": "splitk_reduce", "k_splitk_reduce2": "splitk_reduce", "k_quantize": "quantize_e4m3", "k_fill_zero": "fill_zero",
+               "k_splitk_reduce": "splitk_reduce", "k_splitk_reduce_tiles": "splitk_reduce", "k_quantize": "quantize_e4m3", "k_fill_zero": "fill_zero",
                "k_zero_scalar": "zero_scalar", "k_scale_from_amax": "scale_from_amax", "k_amax_small": "amax_small",
                "k_transpose_weights": "transpose_weights", "k_rmsnorm_fwd": "rmsnorm_fwd", "k_rmsnorm_bwd": "rmsnorm_bwd",
                "k_add_bf16": "add_bf16", "k_sgd_bf16": "sgd_update_bf16", "k_mfma_probe": "mfma_probe",
@@ -96,7 +96,8 @@ def mixed_floor_us(M, d, h, fp8_gemms=1):
 
 
 # the sources the kernels of the timed step are compiled from
-STEP_SOURCES = ("abi.hip", "common.h", "epilogues.h", "gemm.h", "host.h", "launch.h", "mlp_bwd.hip", "mlp_fwd.hip")
+STEP_SOURCES = ("abi.hip", "common.h", "epilogues.h", "gemm.h", "host.h", "launch.h", "mlp_bwd.hip", "mlp_fwd.hip",
+                "persist.h")
 
 
 def kernel_source_hash():
@@ -132,7 +133,7 @@ def summarize_profiles(outdir):
         with open(files[0]) as fh:
             return list(csv.DictReader(fh))
 
-    cmd_bench = "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-extras"
+    cmd_bench = "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-extras --no-graph"
     # kernel trace: per-dispatch durations
     trace = rows("kt", "*kernel_trace.csv")
     dur = {}
@@ -308,6 +309,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the FP8-linear / eval / ablation lines")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay pass (profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (scales the HBM byte counters)")
     ap.add_argument("--hbm-kernels", action="store_true",
@@ -448,24 +450,10 @@ def main():
     # the same step replayed from a HIP graph (two steps per graph, so the
     # forward's amax buffer swap comes back to the captured roles); no entry
     # point allocates, synchronises or reads a device value, so capture holds
-    log("graph replay pass")
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-        step()
-    torch.cuda.synchronize()
-    for _ in range(2):
-        graph.replay()
-    torch.cuda.synchronize()
-    reps = max(1, args.steps // 2)
-    e0.record()
-    for _ in range(reps):
-        graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    graph_ms = e0.elapsed_time(e1) / (2 * reps)
-    del graph
-    log(f"graph replay: {graph_ms:.3f} ms/step")
+    graph_ms = None
+    if not args.no_graph:
+        graph_ms = graph_replay_ms(torch, step, args.steps)
+        log(f"graph replay: {graph_ms:.3f} ms/step")
 
     # matrix-core rate on the workload's own operands (the clock under a dense
     # MFMA load depends on the data; the published peaks assume 2.4 GHz)
@@ -506,9 +494,10 @@ def main():
         "config": {"workload": "relu2_mlp_fwd_bwd_gpt2_small", "M": M, "d": D, "h": H, "margin": MARGIN,
                    "step": "fwd(train)+bwd+W2 cache refresh"},
         "pct_mixed_mfma_peak": round(100.0 * floor_us / (ms * 1e3), 2),
-        "graph_replay": {"ms_per_step": round(graph_ms, 4), "value": round(flops / (graph_ms * 1e-3) / 1e12, 2),
-                         "pct_mixed_mfma_peak": round(100.0 * floor_us / (graph_ms * 1e3), 2),
-                         "steps": 2 * reps, "how": "fwd+bwd+W2 refresh, two steps per captured HIP graph"},
+        "graph_replay": None if graph_ms is None else {
+            "ms_per_step": round(graph_ms, 4), "value": round(flops / (graph_ms * 1e-3) / 1e12, 2),
+            "pct_mixed_mfma_peak": round(100.0 * floor_us / (graph_ms * 1e3), 2),
+            "steps": 2 * max(1, args.steps // 2), "how": "fwd+bwd+W2 refresh, two steps per captured HIP graph"},
         "mixed_mfma_floor_us": round(floor_us, 1),
         "roofline": roofline,
         "mfma_probe": probe,
@@ -517,6 +506,30 @@ def main():
         "extras": extras,
     }
     print(json.dumps(out), flush=True)
+
+
+def graph_replay_ms(torch, step, steps):
+    """The step replayed from a HIP graph: two steps per graph, so the
+    forward's amax buffer swap comes back to the captured roles; no entry
+    point allocates, synchronises or reads a device value, so capture holds."""
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+        step()
+    torch.cuda.synchronize()
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // 2)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (2 * reps)
+    del graph
+    return ms
 
 
 def extra_measurements(fm, torch, dev, X, W1, W2, dY, blk, post, post_q, Y, dX, dW1, dW2, ws_f, ws_b, ws_c,
