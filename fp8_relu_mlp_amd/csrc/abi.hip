@@ -203,48 +203,68 @@ __global__ void k_scale_from_amax(const float* amax, float margin, float* scale_
 }
 
 // ------------------------------------------------------------------ cast-transpose
-// bf16 W [N, K] -> e4m3 Wt [K, N] through a 64 x 64 LDS tile.  The scale is
-// read from scale_in, or computed as 448 / amax (exact policy).
+// bf16 W [N, K] -> e4m3 Wt [K, N] in 128 (n) x kCtBK (k) tiles.  Thread t
+// loads a 4 x (kCtBK / 8) block (rows 4 (t / 8) .. +3, columns
+// (kCtBK / 8) (t % 8) ..: 2 kCtBK bytes of a row per 8 lanes), casts it,
+// transposes it in registers to words of 4 n each and writes those to LDS
+// with 4-byte stores; the tile leaves in rows of 128 codes (16 bytes per
+// lane).  LDS image: row k of 32 words, word c at c ^ (8 ((k / 8) & 3)), so a
+// wave's writes reach 32 banks each twice and its 16-byte reads are
+// conflict-free.  Consecutive blocks take consecutive n-tiles: their rows of
+// Wt continue each other.  The scale is read from scale_in, or computed as
+// 448 / amax (exact policy) from the maxima in amax_part.
+constexpr int kCtBN = 128, kCtBK = 64, kCtKT = kCtBK / 8;
+
+__device__ __forceinline__ uint32_t ct_word(int k, int c) { return (uint32_t)(k * 32 + (c ^ (((k >> 3) & 3) << 3))); }
+
 __global__ void __launch_bounds__(256) k_cast_transpose(const uint16_t* __restrict__ W, int64_t N, int64_t K,
                                                         uint8_t* __restrict__ Wt, const float* scale_in,
                                                         const uint32_t* amax_part, int npart, float* scale_out,
                                                         float* inv_out, float* amax_out) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[64][80];  // [k][n]
+  __shared__ __attribute__((aligned(16))) uint32_t tile[kCtBK * 32];
   __shared__ uint32_t red[4];
-  // every block finishes the amax from the per-block maxima (a few hundred
-  // words) instead of waiting for a separate reduction launch
+  const int tid = (int)threadIdx.x;
   float amax = 0.0f;
   if (amax_part) {
     uint32_t m = 0;
-    for (int i = threadIdx.x; i < npart; i += 256) m = amax_part[i] > m ? amax_part[i] : m;
+    for (int i = tid; i < npart; i += 256) m = amax_part[i] > m ? amax_part[i] : m;
     amax = __uint_as_float(block_max_u32(m, red));
   }
   const float s = scale_in ? *scale_in : scale_from_amax(amax, 1.0f);
-  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
+  const int64_t n0 = (int64_t)blockIdx.x * kCtBN, k0 = (int64_t)blockIdx.y * kCtBK;
+  const int rg = tid >> 3, kg = tid & 7;
+  // 1. the block, cast: w[r][h] holds columns kCtKT kg + 4 h .. +3 of row 4 rg + r
+  uint32_t w[4][kCtKT / 4];
 #pragma unroll
-  for (int it = 0; it < 2; it++) {
-    const int c = threadIdx.x + it * 256;
-    const int r = c >> 3, ch = c & 7;
-    const int64_t n = n0 + r, k = k0 + ch * 8;
-    if (n < N && k < K) {
-      const uint4 v = *(const uint4*)(W + n * K + k);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      const uint32_t lo = pack_e4m3x4(bf16_lo(w[0]) * s, bf16_hi(w[0]) * s, bf16_lo(w[1]) * s, bf16_hi(w[1]) * s);
-      const uint32_t hi = pack_e4m3x4(bf16_lo(w[2]) * s, bf16_hi(w[2]) * s, bf16_lo(w[3]) * s, bf16_hi(w[3]) * s);
+  for (int r = 0; r < 4; r++) {
+    const int64_t n = n0 + 4 * rg + r;
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        tile[ch * 8 + e][r] = (uint8_t)(lo >> (8 * e));
-        tile[ch * 8 + 4 + e][r] = (uint8_t)(hi >> (8 * e));
-      }
+    for (int q = 0; q < kCtKT / 8; q++) {
+      const int64_t k = k0 + kCtKT * kg + 8 * q;
+      uint4 v = uint4{0, 0, 0, 0};
+      if (n < N && k < K) v = *(const uint4*)(W + n * K + k);
+      w[r][2 * q] = pack_e4m3x4(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
+      w[r][2 * q + 1] = pack_e4m3x4(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
     }
   }
-  __syncthreads();
-  {
-    const int r = threadIdx.x >> 2, ch = threadIdx.x & 3;
-    const int64_t k = k0 + r, n = n0 + ch * 16;
-    if (k < K && n < N) *(uint4*)(Wt + k * N + n) = *(const uint4*)&tile[r][ch * 16];
+  // 2. transposed: column kCtKT kg + j, rows 4 rg .. +3 -> one word
+#pragma unroll
+  for (int j = 0; j < kCtKT; j++) {
+    const int h = j >> 2, b = 8 * (j & 3);
+    const uint32_t o = ((w[0][h] >> b) & 0xffu) | (((w[1][h] >> b) & 0xffu) << 8) | (((w[2][h] >> b) & 0xffu) << 16) |
+                       (((w[3][h] >> b) & 0xffu) << 24);
+    tile[ct_word(kCtKT * kg + j, rg)] = o;
   }
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+  __syncthreads();
+  // 3. rows of Wt: kCtBK k x 8 chunks of 16 n
+#pragma unroll
+  for (int it = 0; it < kCtBK / 32; it++) {
+    const int i = tid + it * 256, k = i >> 3, ch = i & 7;
+    const int64_t kk = k0 + k, n = n0 + ch * 16;
+    const uint4 v = *(const uint4*)&tile[ct_word(k, 4 * ch)];
+    if (kk < K && n < N) *(uint4*)(Wt + kk * N + n) = v;
+  }
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     if (scale_out) *scale_out = s;
     if (inv_out) *inv_out = 1.0f / s;
     if (amax_out) *amax_out = amax;
@@ -363,7 +383,14 @@ int fp8_cast_transpose(const uint16_t* W, int64_t N, int64_t K, uint8_t* Wt_q, c
     part = N * K <= kAmaxSmall ? (uint32_t*)workspace : (uint32_t*)((char*)workspace + 256);
     FP8MLP_TRY(launch_amax_partials(FP8MLP_BF16, W, N * K, part, &npart, st));
   }
-  dim3 grid((unsigned)cdiv(K, 64), (unsigned)cdiv(N, 64));
+  dim3 grid((unsigned)cdiv(N, kCtBN), (unsigned)cdiv(K, kCtBK));
+  if (npart > 1 && (int64_t)grid.x * grid.y * npart > (int64_t)1 << 20) {
+    // a large weight: one block finishes the maximum once (into the
+    // workspace's first word) instead of every block re-reading the partials
+    FP8MLP_TRY(launch_max_small((const float*)part, npart, (float*)workspace, nullptr, 0.0f, nullptr, st));
+    part = (uint32_t*)workspace;
+    npart = 1;
+  }
   TraceScope trace("cast_transpose", st);
   hipLaunchKernelGGL(k_cast_transpose, grid, dim3(256), 0, st, W, N, K, Wt_q, scale_in, (const uint32_t*)part, npart,
                      scale_out, inv_scale_out, amax_out);
