@@ -23,6 +23,7 @@ SIGNATURES = {
     "fp8mlp_abi_version": (c_int, []),
     "fp8mlp_status_str": (ctypes.c_char_p, [c_int]),
     "fp8mlp_last_hip_error": (c_int, []),
+    "fp8mlp_last_failed_kernel": (ctypes.c_char_p, []),
     "mlp_relu2_fwd_workspace": (c_size, [c_i64, c_i64, c_i64]),
     "mlp_relu2_fwd": (c_int, [c_int, vp, vp, vp, vp, vp, vp, c_float, vp, vp, vp, vp, vp,
                               c_i64, c_i64, c_i64, vp, c_size, vp]),
@@ -94,4 +95,7 @@ def check(name, status):
         msg = lib().fp8mlp_status_str(status).decode()
         if status == -6:
             msg += f" (hipError_t {lib().fp8mlp_last_hip_error()})"
+            failed = lib().fp8mlp_last_failed_kernel()
+            if failed:
+                msg += f" in kernel {failed.decode()}"
         raise Fp8MlpError(name, status, msg)

@@ -26,8 +26,16 @@ inline int hip_status(hipError_t e) {
   g_last_hip_error = (int)e;
   return FP8MLP_E_HIP;
 }
+// FP8MLP_SYNC_CHECK=1 debug mode (trace.hip): after a launch, wait for the
+// launching stream and report a failure of that kernel as FP8MLP_E_HIP,
+// naming it for fp8mlp_last_failed_kernel().
+int sync_check();
+bool sync_check_on();
 // Status of the most recent kernel launch on this thread.
-inline int launch_status() { return hip_status(hipGetLastError()); }
+inline int launch_status() {
+  const int st = hip_status(hipGetLastError());
+  return st == FP8MLP_OK && sync_check_on() ? sync_check() : st;
+}
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

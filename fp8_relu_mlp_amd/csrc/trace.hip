@@ -4,6 +4,7 @@
 // cross-check the rocprofv3 kernel trace.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <vector>
 
 #include "host.h"
@@ -22,9 +23,39 @@ struct TraceState {
   int dropped = 0;
 };
 thread_local TraceState g_trace;
+// the launch in progress on this thread (set between a TraceScope's
+// construction and destruction) and the last kernel the sync check saw fail
+thread_local const char* g_cur_name = nullptr;
+thread_local hipStream_t g_cur_stream = nullptr;
+thread_local bool g_cur_set = false;
+thread_local const char* g_failed_kernel = nullptr;
 }  // namespace
 
+bool sync_check_on() {
+  const char* e = std::getenv("FP8MLP_SYNC_CHECK");
+  return e != nullptr && e[0] == '1';
+}
+
+int sync_check() {
+  hipError_t e = hipSuccess;
+  if (g_cur_set) {
+    // never under graph capture: a capturing stream cannot be waited on
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(g_cur_stream, &cs);
+    if (e == hipSuccess && cs != hipStreamCaptureStatusNone) return FP8MLP_OK;
+    if (e == hipSuccess) e = hipStreamSynchronize(g_cur_stream);
+  } else {
+    e = hipDeviceSynchronize();
+  }
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) g_failed_kernel = g_cur_set ? g_cur_name : "(launch outside a named scope)";
+  return hip_status(e);
+}
+
 TraceScope::TraceScope(const char* name, hipStream_t s) : stream_(s), slot_(-1) {
+  g_cur_name = name;
+  g_cur_stream = s;
+  g_cur_set = true;
   TraceState& t = g_trace;
   if (!t.on) return;
   if (t.used >= (int)t.pool.size()) {
@@ -37,6 +68,7 @@ TraceScope::TraceScope(const char* name, hipStream_t s) : stream_(s), slot_(-1) 
 }
 
 TraceScope::~TraceScope() {
+  g_cur_set = false;
   if (slot_ >= 0) (void)hipEventRecord(g_trace.pool[slot_].end, stream_);
 }
 
@@ -78,5 +110,7 @@ int fp8mlp_timing_get(int i, const char** name, float* ms) {
 }
 
 int fp8mlp_timing_dropped(void) { return g_trace.dropped; }
+
+const char* fp8mlp_last_failed_kernel(void) { return g_failed_kernel; }
 
 }  // extern "C"

@@ -66,6 +66,12 @@ int fp8mlp_abi_version(void);
 const char* fp8mlp_status_str(int status);
 /* hipError_t value behind the last FP8MLP_E_HIP returned on this thread. */
 int fp8mlp_last_hip_error(void);
+/* Debug mode: with the environment variable FP8MLP_SYNC_CHECK=1, every launch
+ * of the library waits for its stream (not under graph capture) and a kernel
+ * that failed is reported as FP8MLP_E_HIP by the call that launched it;
+ * fp8mlp_last_failed_kernel() then names that kernel (NULL if none failed on
+ * this thread).  The name is a static string owned by the library. */
+const char* fp8mlp_last_failed_kernel(void);
 
 /* ------------------------------------------------------------------------
  * mlp_relu2_fwd -- one forward of the MLP block.

@@ -68,6 +68,12 @@ def test_library_exports_every_declared_symbol(L):
     assert not missing, missing
 
 
+def test_no_failed_kernel_before_any_launch(L):
+    """fp8mlp_last_failed_kernel() (FP8MLP_SYNC_CHECK=1 debug mode) names
+    nothing until a checked launch has failed on this thread."""
+    assert L.fp8mlp_last_failed_kernel() is None
+
+
 def test_binding_covers_the_header(L):
     from fp8_relu_mlp_amd import _lib
     assert sorted(_lib.SIGNATURES) == declared()
