@@ -271,10 +271,15 @@ def measured_traffic():
     return {k: v["fetch_bytes"] + v["write_bytes"] for k, v in t.get("kernels", {}).items()}
 
 
-def cpu_baseline(ins, amax_prev, chunk=4096):
+def cpu_baseline(ins, amax_prev, gpu=None, chunk=4096):
     """The oracle (as it stands) on the whole workload: all M token rows of
     fwd (TRAIN) + bwd + the W2 cache refresh, in row chunks of ``chunk`` (the
-    weight gradients summed over the chunks) to bound host memory."""
+    weight gradients summed over the chunks) to bound host memory.
+
+    With ``gpu`` (the GPU's Y, dX, dW1, dW2 and post_q of one step from the
+    same inputs and amax_prev), the oracle's outputs are also compared with
+    them (relative Frobenius errors, share of differing e4m3 codes); the
+    comparison time is not part of the timed baseline."""
     import numpy as np
     from oracle import formats as F
     from oracle import mlp as O
@@ -285,6 +290,14 @@ def cpu_baseline(ins, amax_prev, chunk=4096):
         blas = 1
     cores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
+    t_cmp = 0.0
+    err = {"Y": [0.0, 0.0], "dX": [0.0, 0.0]}
+    mismatch = 0
+
+    def as_f64(a):
+        a = np.asarray(a)
+        return F.bf16_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
     W2t, _, inv_sw, _ = O.cast_transpose(ins["W2"])
     dW1 = np.zeros((H, D))
     dW2 = np.zeros((D, H))
@@ -294,12 +307,30 @@ def cpu_baseline(ins, amax_prev, chunk=4096):
         bw = O.mlp_bwd(ins["dY"][r0:r1], ins["X"][r0:r1], ins["W1"], ins["W2"], F.bf16_to_f64(out["post"]))
         dW1 += bw["dW1"]
         dW2 += bw["dW2"]
-    t = time.perf_counter() - t0
+        if gpu is not None:
+            tc = time.perf_counter()
+            for k, ref in (("Y", out["y"]), ("dX", bw["dX"])):
+                r, g = as_f64(ref), as_f64(gpu[k][r0:r1])
+                err[k][0] += float(np.sum((g - r) ** 2))
+                err[k][1] += float(np.sum(r ** 2))
+            mismatch += int(np.count_nonzero(np.asarray(out["post_q"]) != gpu["post_q"][r0:r1]))
+            t_cmp += time.perf_counter() - tc
+    t = time.perf_counter() - t0 - t_cmp
+    parity = None
+    if gpu is not None:
+        rel = {k: (v[0] / v[1]) ** 0.5 if v[1] > 0 else 0.0 for k, v in err.items()}
+        for k, ref in (("dW1", dW1), ("dW2", dW2)):
+            rel[k] = float(np.linalg.norm(gpu[k].astype(np.float64) - ref) / np.linalg.norm(ref))
+        gates = {"Y": 2e-2, "dX": 1e-2, "dW1": 1e-2, "dW2": 1e-2}
+        parity = {"rel_fro": {k: round(v, 6) for k, v in rel.items()}, "gates": gates,
+                  "post_q_codes_differing": mismatch / float(M * H),
+                  "pass": all(rel[k] <= g for k, g in gates.items()),
+                  "against": "the oracle run on its own from X, W1, W2, dY and the step's amax_prev"}
     # cores: the threads the oracle's BLAS calls ran on (its other numpy steps run on one)
     return {"value": 12.0 * M * D * H / t / 1e12, "unit": "TFLOP/s", "cores": blas, "kind": "oracle",
             "sample": f"the whole workload: all {M} token rows (d={D}, h={H}), fwd+bwd+W2 refresh, in row chunks "
                       f"of {chunk}, {t:.1f} s", "seconds": round(t, 2), "blas_threads": blas,
-            "affinity_cores": cores}
+            "affinity_cores": cores, "parity": parity}
 
 
 def main():
@@ -310,6 +341,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the FP8-linear / eval / ablation lines")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay pass (profiler runs)")
+    ap.add_argument("--jsonl", metavar="PATH",
+                    help="also append the record, with host cores, GPU identity and clocks, to this JSONL file")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (scales the HBM byte counters)")
     ap.add_argument("--hbm-kernels", action="store_true",
@@ -484,8 +517,16 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
+        # one more step whose outputs the oracle's are compared with
+        amax_used = float(blk.amax_prev.item())
+        blk.forward(X, post=post, post_q=post_q, Y=Y, workspace=ws_f)
+        blk.backward(dY, X, post, dX, dW1, dW2, workspace=ws_b)
+        torch.cuda.synchronize()
+        u16 = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+        gpu_out = {"Y": u16(Y), "dX": u16(dX), "dW1": dW1.cpu().numpy(), "dW2": dW2.cpu().numpy(),
+                   "post_q": post_q.cpu().numpy()}
         log("cpu baseline (the oracle on the whole workload)")
-        cpu = cpu_baseline(ins, float(blk.amax_prev.item()))
+        cpu = cpu_baseline(ins, amax_used, gpu_out)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -506,6 +547,40 @@ def main():
         "extras": extras,
     }
     print(json.dumps(out), flush=True)
+    if args.jsonl:
+        rec = dict(out, time_utc=time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime()), host=host_info(),
+                   gpu=gpu_info(torch))
+        with open(args.jsonl, "a") as fh:
+            fh.write(json.dumps(rec) + "\n")
+
+
+def host_info():
+    info = {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count(),
+            "python": sys.version.split()[0]}
+    try:
+        from threadpoolctl import threadpool_info
+        info["blas_threads"] = max([p.get("num_threads", 1) for p in threadpool_info()
+                                    if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        pass
+    return info
+
+
+def gpu_info(torch):
+    """Identity of GPU 0 and its shader-clock levels as the driver lists them
+    (sysfs pp_dpm_sclk, the current level marked *), where readable."""
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2**30, 1), "torch": torch.__version__,
+            "hip": getattr(torch.version, "hip", None)}
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(f) as fh:
+                info["sclk_levels"] = [ln.strip() for ln in fh if ln.strip()]
+            break
+        except OSError:
+            continue
+    return info
 
 
 def graph_replay_ms(torch, step, steps):
