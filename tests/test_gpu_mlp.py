@@ -207,8 +207,10 @@ def run_bwd(fm, ins, post_bits, accumulate=False, dW_init=None):
     return bits(dX), dW1.cpu().numpy().astype(np.float64), dW2.cpu().numpy().astype(np.float64)
 
 
+# (8100, 256, 2944): 32 x 12 = 384 dgrad tiles, more than the 256 blocks of
+# the persistent kernel, with a ragged last tile row and column
 @pytest.mark.parametrize("M,d,h", [(256, 128, 512), (1, 64, 128), (300, 192, 384), (1000, 768, 3072),
-                                   (2500, 256, 512)])
+                                   (2500, 256, 512), (8100, 256, 2944)])
 def test_bwd_parity(fm, M, d, h):
     ins = synth.mlp_inputs(M, d, h, 60 + M, with_dy=True)
     case(f"bwd fwd-pass M={M} d={d} h={h}")
