@@ -119,6 +119,10 @@ struct GemmArgs {
   int64_t k_per_split;  // multiple of BK
   int stagger;          // > 0: blocks of the second residency slot start ~stagger x 4 us late
   int group_m;          // tile rows per group of the tile order (set by launch_gemm)
+  // > 0: a row-contiguous P operand has only rows k < p_rows (K is padded up
+  // to a whole k-tile and the A operand carries zeros there); the loads of
+  // rows past it return zeros
+  int64_t p_rows;
   // Optional side job for wave 0 of block 0 (red_in != nullptr): the
   // maximum of red_n fp32 values >= +0 or NaN, given as bit patterns, ->
   // *red_out, and, if red_scale_out is set, the scale of *red_amax_prev and
@@ -353,7 +357,9 @@ struct TileLoads {
     if constexpr (C::PL == KC) {
       rp = make_rsrc(p + t.n0 * ldp_b + t.kb * C::PELT, (uint64_t)((a.N - t.n0) * ldp_b - t.kb * C::PELT));
     } else {
-      rp = make_rsrc(p + t.kb * ldp_b + t.n0 * C::PELT, (uint64_t)((t.ke - t.kb) * ldp_b - t.n0 * C::PELT));
+      const int64_t pke = a.p_rows > 0 && a.p_rows < t.ke ? a.p_rows : t.ke;
+      const int64_t pbytes = (pke - t.kb) * ldp_b - t.n0 * C::PELT;
+      rp = make_rsrc(p + t.kb * ldp_b + t.n0 * C::PELT, (uint64_t)(pbytes > 0 ? pbytes : 0));
     }
 #pragma unroll
     for (int j = 0; j < C::Q_LOADS; j++)
