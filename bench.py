@@ -43,7 +43,8 @@ KID_NAMES = {1: "up_gemm_relu2_quant", 2: "down_gemm_e4m3", 3: "down_gemm_bf16_e
              10: "ce_head_gemm_stats", 11: "ce_head_gemm_grad", 12: "ce_dx_gemm", 13: "ce_dw_gemm",
              14: "ce_head_gemm_e4m3_stats", 15: "ce_head_gemm_e4m3_grad", 16: "dw_gemm"}
 OTHER_NAMES = {"k_max_final": "amax_final", "k_amax_partial": "amax_partial", "k_cast_transpose": "cast_transpose",
-               "k_splitk_reduce": "splitk_reduce", "k_splitk_reduce_tiles": "splitk_reduce", "k_quantize": "quantize_e4m3", "k_fill_zero": "fill_zero",
+               "k_splitk_reduce": "splitk_reduce", "k_splitk_reduce_tiles": "splitk_reduce", "k_quantize": "quantize_e4m3",
+               "k_lin_panel": "fp8_linear_panel", "k_fill_zero": "fill_zero",
                "k_zero_scalar": "zero_scalar", "k_scale_from_amax": "scale_from_amax", "k_amax_small": "amax_small",
                "k_transpose_weights": "transpose_weights", "k_rmsnorm_fwd": "rmsnorm_fwd", "k_rmsnorm_bwd": "rmsnorm_bwd",
                "k_add_bf16": "add_bf16", "k_sgd_bf16": "sgd_update_bf16", "k_mfma_probe": "mfma_probe",
@@ -80,7 +81,7 @@ def hbm_kernel_bytes(M, d, h):
         "amax_partial": M * h * 2,                  # max |x| over a [M, h] bf16 tensor (post-sized)
         "cast_transpose": M * h * 2 + M * h,        # [M, h] bf16 -> [h, M] e4m3, given scale
         "count_top_codes": M * h,                   # e4m3 codes at 448 in a [M, h] tensor
-        "quantize_e4m3": M * d * 2 + M * d,         # X [M, d] bf16 -> e4m3 (fp8_linear's first step)
+        "quantize_e4m3": M * d * 2 + M * d,         # X [M, d] bf16 -> e4m3 (fp8_linear's pass for K > 768)
     }
 
 
@@ -119,6 +120,45 @@ def logical_kernel_name(raw):
     if m:
         return OTHER_NAMES.get(m.group(1), m.group(1))
     return raw
+
+
+def linear_work(M, d, n):
+    """fp8_linear at M x d -> n: flops and algorithmic HBM bytes (X read once in bf16, the e4m3 weight,
+    Y written in bf16) of one call."""
+    return 2.0 * M * d * n, M * d * 2 + d * n + M * n * 2
+
+
+def summarize_linear(outdir):
+    """profiles/kernel_trace_fp8_linear_M49152.md from rocprofv3 kernel traces of `bench.py --linear qkv`
+    and `--linear o` under outdir/lin_qkv and outdir/lin_o."""
+    cmd = "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/lin_{p} -o k -- python3 bench.py --linear {p}"
+    lines = ["# fp8_linear kernel durations: the QKV and output projections, M=49152, K=768 (one MI355X)", "",
+             "Commands (from a scratch directory, TMPDIR=/tmp):", "", "    " + cmd.format(p="qkv"),
+             "    " + cmd.format(p="o"), "",
+             "Summarised with `python3 bench.py --summarize-linear OUT`.  Seven calls per run (the first two",
+             "are warm-up, left out below).  Algorithmic bytes: X read once in bf16, the e4m3 weight, Y written",
+             "in bf16.  Roofline time = max(flops / 5.0 PFLOP/s, bytes / 8 TB/s); fraction = roofline time /",
+             "measured time.", "",
+             "| projection | N | kernel | calls | avg us | TFLOP/s | of fp8 peak | GB/s alg. | of roofline |",
+             "|---|---:|---|---:|---:|---:|---:|---:|---:|"]
+    for proj, n in (("qkv", 3 * D), ("o", D)):
+        files = sorted(glob.glob(os.path.join(outdir, f"lin_{proj}", "**", "*kernel_trace.csv"), recursive=True))
+        if not files:
+            raise SystemExit(f"no kernel trace under {os.path.join(outdir, 'lin_' + proj)}")
+        with open(files[0]) as fh:
+            trace = list(csv.DictReader(fh))
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
+                if logical_kernel_name(r["Kernel_Name"]) == "fp8_linear_panel"][2:]
+        if not durs:
+            raise SystemExit(f"no fp8_linear_panel dispatch in {files[0]}")
+        avg = sum(durs) / len(durs)
+        fl, by = linear_work(M, D, n)
+        roof = max(fl / (PEAK_FP8 * 1e12), by / (PEAK_HBM * 1e9)) * 1e6
+        lines.append(f"| {proj} | {n} | fp8_linear_panel | {len(durs)} | {avg:.1f} | {fl / avg / 1e6:.0f} | "
+                     f"{fl / avg / 1e6 / PEAK_FP8:.3f} | {by / avg / 1e3:.0f} | {roof / avg:.3f} |")
+    with open(os.path.join(PROFILES, "kernel_trace_fp8_linear_M49152.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {PROFILES}/kernel_trace_fp8_linear_M49152.md")
 
 
 def summarize_profiles(outdir):
@@ -214,7 +254,8 @@ def summarize_profiles(outdir):
                  "Command (from a scratch directory, TMPDIR=/tmp):", "", f"    {cmd}", "",
                  f"Sizes: M={M}, d={D}, h={H}. amax_partial: max |x| over a [M, h] bf16 tensor; cast_transpose:",
                  "[M, h] bf16 -> [h, M] e4m3 with a given scale; count_top_codes: the e4m3 codes at 448 in a",
-                 "[M, h] tensor; quantize_e4m3: X [M, d] bf16 -> e4m3 (the first step of fp8_linear). GB/s =",
+                 "[M, h] tensor; quantize_e4m3: X [M, d] bf16 -> e4m3 (fp8_linear's conversion pass, which it",
+                 "runs for K > 768: here X viewed as [M/2, 2d]; also the first step of the e4m3 up-projection). GB/s =",
                  f"algorithmic bytes per launch / average duration; peak HBM {PEAK_HBM / 1e3:.0f} TB/s.", "",
                  "| kernel | launches | avg us | algorithmic MB | GB/s | of peak |", "|---|---:|---:|---:|---:|---:|"]
         ours = set(OTHER_NAMES.values()) | set(KID_NAMES.values())
@@ -348,9 +389,18 @@ def main():
     ap.add_argument("--hbm-kernels", action="store_true",
                     help="only run the bandwidth-bound kernels at the workload's large sizes, 5 launches each "
                          "(for a rocprofv3 kernel trace)")
+    ap.add_argument("--linear", choices=("qkv", "o"),
+                    help="only run fp8_linear on the QKV or output projection (M=49152, K=768), 2 + 5 calls "
+                         "(for a rocprofv3 kernel trace)")
+    ap.add_argument("--summarize-linear", metavar="OUT",
+                    help="write profiles/kernel_trace_fp8_linear_M49152.md from the rocprofv3 runs of --linear "
+                         "under OUT/lin_qkv and OUT/lin_o (no GPU needed)")
     ap.add_argument("--summarize-profiles", metavar="OUT",
                     help="write the profiles/ summaries from the rocprofv3 runs under OUT (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_linear:
+        summarize_linear(args.summarize_linear)
+        return
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles)
         return
@@ -389,10 +439,11 @@ def main():
         q = torch.empty((H, M), dtype=torch.uint8, device=dev)
         cnt = torch.zeros(1, dtype=torch.int64, device=dev)
         ws_t = torch.empty(max(1, fm.lib().fp8_saturation_count_workspace(M * H)), dtype=torch.uint8, device=dev)
-        wt = torch.zeros((D, D), dtype=torch.uint8, device=dev)
+        # fp8_linear with K = 2d > 768 runs its conversion pass over all of X, then a narrow GEMM
+        wt = torch.zeros((2 * D, 64), dtype=torch.uint8, device=dev)
         winv = f1(1.0)
-        yl = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
-        ws_l = torch.empty(max(1, fm.lib().fp8_linear_workspace(M, D)), dtype=torch.uint8, device=dev)
+        yl = torch.empty((M // 2, 64), dtype=torch.bfloat16, device=dev)
+        ws_l = torch.empty(max(1, fm.lib().fp8_linear_workspace(M // 2, 2 * D)), dtype=torch.uint8, device=dev)
         for _ in range(5):
             fm.amax_reduce(big, amx, workspace=ws_a)
         for _ in range(5):
@@ -400,9 +451,30 @@ def main():
         for _ in range(5):
             fm.fp8_saturation_count(q, cnt, workspace=ws_t)
         for _ in range(5):
-            fm.fp8_linear(xs, sx, wt, winv, yl, x_amax_out=xam, workspace=ws_l)
+            fm.fp8_linear(xs.view(M // 2, 2 * D), sx, wt, winv, yl, x_amax_out=xam, workspace=ws_l)
         torch.cuda.synchronize()
         print(json.dumps({"bytes_per_launch": hbm_kernel_bytes(M, D, H), "launches": 5}))
+        return
+    if args.linear:
+        a = synth.attn_inputs()
+        xk, wk, n = ("X", "Wqkv", 3 * D) if args.linear == "qkv" else ("Xo", "Wo", D)
+
+        def bf1(x):
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        Xa, Wa = bf1(a[xk]), bf1(a[wk])
+        Wt = torch.empty((D, n), dtype=torch.uint8, device=dev)
+        f1 = lambda v=0.0: torch.full((1,), v, dtype=torch.float32, device=dev)
+        inv_w, amax, sx = f1(), f1(), f1()
+        fm.fp8_cast_transpose(Wa, Wt, inv_scale_out=inv_w)
+        fm.amax_reduce(Xa, amax)
+        fm.fp8_scale_from_amax(amax, 1.0, sx)
+        Ya = torch.empty((Xa.shape[0], n), dtype=torch.bfloat16, device=dev)
+        wsl = torch.empty(max(1, fm.lib().fp8_linear_workspace(Xa.shape[0], D)), dtype=torch.uint8, device=dev)
+        for _ in range(7):
+            fm.fp8_linear(Xa, sx, Wt, inv_w, Ya, workspace=wsl)
+        torch.cuda.synchronize()
+        print(json.dumps({"projection": args.linear, "M": int(Xa.shape[0]), "K": D, "N": n, "calls": 7}))
         return
     log("generating inputs")
     ins = synth.mlp_inputs(M, D, H, synth.WORKLOADS["fwdbwd"][3], with_dy=True)
@@ -897,9 +969,10 @@ def extra_measurements(fm, torch, dev, X, W1, W2, dY, blk, post, post_q, Y, dX, 
         Ya = torch.empty((Xa.shape[0], n), dtype=torch.bfloat16, device=dev)
         wsl = torch.empty(max(1, fm.lib().fp8_linear_workspace(Xa.shape[0], D)), dtype=torch.uint8, device=dev)
         t = timed(lambda: fm.fp8_linear(Xa, sx, Wt, inv_w, Ya, workspace=wsl))
-        fl = 2.0 * Xa.shape[0] * D * n
-        by = Xa.shape[0] * D * 2 + D * n + Xa.shape[0] * n * 2
+        fl, by = linear_work(Xa.shape[0], D, n)
+        roof_ms = max(fl / (PEAK_FP8 * 1e12), by / (PEAK_HBM * 1e9)) * 1e3
         out[f"fp8_linear_{tag}_us"] = round(t * 1e3, 2)
+        out[f"fp8_linear_{tag}_frac_roofline"] = round(roof_ms / t, 4)
         out[f"fp8_linear_{tag}_tflops"] = round(fl / (t * 1e-3) / 1e12, 1)
         out[f"fp8_linear_{tag}_frac_fp8_peak"] = round(fl / (t * 1e-3) / 1e12 / PEAK_FP8, 4)
         out[f"fp8_linear_{tag}_hbm_gbs_alg"] = round(by / (t * 1e-3) / 1e9, 1)

@@ -256,10 +256,13 @@ int fp8_saturation_count(const uint8_t* q, int64_t n, uint64_t* count_out, void*
  * x_scale, w_inv_scale: device fp32.  x_amax_out: device fp32 or NULL; if
  * given it receives max |X| (for the next step's delayed scale); it must not
  * be x_scale or w_inv_scale (E_ARG), which the same launch still reads.
- * K and N: positive multiples of 64; M >= 0.
- * workspace: fp8_linear_workspace(M, K) bytes (the e4m3 copy of X, its rows
- * padded with zero codes to a multiple of 128, and the conversion's
- * per-block maxima of |X|).
+ * K and N: positive multiples of 64; M >= 0.  For K <= 768 one launch
+ * converts each row of X inside the GEMM and keeps the codes on chip; for
+ * larger K a conversion pass writes the e4m3 copy of X to the workspace
+ * first.  Both give the same Y.
+ * workspace: fp8_linear_workspace(M, K) bytes (room for the e4m3 copy of X,
+ * its rows padded with zero codes to a multiple of 128, used when K > 768,
+ * and for the per-block maxima of |X|).
  * ---------------------------------------------------------------------- */
 size_t fp8_linear_workspace(int64_t M, int64_t K);
 int fp8_linear(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, const float* w_inv_scale,

@@ -48,9 +48,14 @@ def run_linear(fm, Xb, Wb, margin=1.0, scale_in=None):
     return {"Y": bits(Y), "sx": sx.item(), "inv_w": inv_w.item(), "Wt": Wt.cpu().numpy(), "xamax": xam.item()}
 
 
-# K = 64, 320: not whole 128-code k-tiles (the e4m3 copy of X is padded)
+# K = 64, 320: not whole 128-code k-tiles (the e4m3 rows are padded).  K <=
+# 768 runs the row-panel kernel: (8192, 768, 2304) and (40000, 128, 512) give
+# its blocks several output tiles each, with changes of row panel inside a
+# block (the second with two 64-k tiles per output tile); (3000, 768, 320)
+# has a part-filled last column tile.  K = 1024 runs the two-launch path.
 @pytest.mark.parametrize("M,K,N", [(1000, 768, 2304), (777, 768, 768), (1, 128, 64), (300, 256, 192),
-                                   (513, 64, 128), (1000, 320, 576)])
+                                   (513, 64, 128), (1000, 320, 576), (8192, 768, 2304), (40000, 128, 512),
+                                   (3000, 768, 320), (600, 1024, 256)])
 def test_fp8_linear_parity(fm, M, K, N):
     case(f"fp8_linear M={M} K={K} N={N}")
     a = synth.attn_inputs(M=M, d=K, qkv=N, seed=90 + M)
