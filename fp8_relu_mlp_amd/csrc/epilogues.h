@@ -59,14 +59,16 @@ struct Tile16 {
   }
   // The same sweep for a tile that lies wholly inside the matrix, without
   // bounds checks: f(p, 16 bytes) for pass p, in which this thread holds
-  // tile row row0() + p * ROWS_PER_PASS, chunk chunk0().
+  // tile row row0() + p * ROWS_PER_PASS, chunk chunk0().  Needs whole rows
+  // per pass, a multiple of the swizzle period apart (WHOLE); other tiles
+  // (384 columns: 48 chunks a row) store through the general sweep.
   static constexpr int ROWS_PER_PASS = C::NT / CPR;
-  static_assert(C::NT % CPR == 0, "whole rows per pass");
-  static_assert(ROWS_PER_PASS % (XM + 1) == 0, "passes keep the row swizzle");
+  static constexpr bool WHOLE = C::NT % CPR == 0 && ROWS_PER_PASS % (XM + 1) == 0;
   __device__ static __forceinline__ int row0() { return (int)threadIdx.x / CPR; }
   __device__ static __forceinline__ int chunk0() { return (int)threadIdx.x % CPR; }
   template <class F>
   __device__ static __forceinline__ void rows_interior(const FP8MLP_LDS char* s, F&& f) {
+    static_assert(WHOLE, "whole rows per pass, keeping the row swizzle");
     const uint32_t o = off(row0(), chunk0());
 #pragma unroll
     for (int p = 0; p < PASSES; p++) {
@@ -78,14 +80,16 @@ struct Tile16 {
   // The LDS image -> the 16-bit matrix g (leading dimension ld), row by row,
   // with streaming stores; tiles inside the matrix skip the bounds checks.
   __device__ static __forceinline__ void store(const FP8MLP_LDS char* s, const TileCtx& c, uint16_t* g, int64_t ld) {
-    if (c.m0 + C::BM <= c.M && c.n0 + C::BN <= c.N) {
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(g + c.m0 * ld + c.n0, (uint64_t)C::BM * ld * 2);
-      const uint32_t o = (uint32_t)row0() * (uint32_t)ld * 2 + chunk0() * 16;
-      const uint32_t step = (uint32_t)ROWS_PER_PASS * (uint32_t)ld * 2;
-      rows_interior(s, [&](int p, uint4 v) { buffer_store_stream16(r, o + p * step, v); });
-    } else {
-      rows(s, c, [&](int64_t m, int64_t n, uint4 v) { store_stream(g + m * ld + n, v); });
+    if constexpr (WHOLE) {
+      if (c.m0 + C::BM <= c.M && c.n0 + C::BN <= c.N) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(g + c.m0 * ld + c.n0, (uint64_t)C::BM * ld * 2);
+        const uint32_t o = (uint32_t)row0() * (uint32_t)ld * 2 + chunk0() * 16;
+        const uint32_t step = (uint32_t)ROWS_PER_PASS * (uint32_t)ld * 2;
+        rows_interior(s, [&](int p, uint4 v) { buffer_store_stream16(r, o + p * step, v); });
+        return;
+      }
     }
+    rows(s, c, [&](int64_t m, int64_t n, uint4 v) { store_stream(g + m * ld + n, v); });
   }
   // Global 16-bit matrix (leading dimension ld) -> LDS image, loaded straight
   // into LDS in row order (streaming: read once); rows past the matrix end

@@ -13,9 +13,10 @@ namespace fp8mlp {
 // ahead (three X buffers: 160 KB of LDS).
 using CfgUp = GemmCfg<2, 256, 256, 128, 2, 1, KC, KC, 0, 8, 0, 3>;
 // post_q [M,h] . W2t_q [h,d] : e4m3, the cache is read with transposing LDS
-// loads; 192 x 256 two-group tiles (d = 768 is three of them, M = 49152 three
-// rounds of 256 blocks), three post_q buffers.
-using CfgDown8 = GemmCfg<1, 192, 256, 128, 2, 1, KC, MNC, 0, 8, 0, 3>;
+// loads; 192 x 384 two-group tiles (d = 768 is two of them, M = 49152 two
+// rounds of 256 blocks; nine MFMAs per phase and wave), two post_q buffers
+// (a third does not fit beside the 48 KB W2t_q tiles).
+using CfgDown8 = GemmCfg<1, 192, 384, 128, 2, 1, KC, MNC, 0, 8, 0, 2>;
 // Xq [M,d] . W1t_q [d,h] : the up-projection in e4m3 (the W1 cache is read
 // with transposing LDS loads), 256 x 256 tiles, two groups of four waves,
 // three Xq buffers.
