@@ -98,3 +98,36 @@ def test_fp8_linear_empty(fm):
     fm.fp8_linear(X, f32_dev(1.0), Wt, f32_dev(1.0), Y, am)
     torch.cuda.synchronize()
     assert am.item() == 0.0
+
+
+@pytest.mark.parametrize("with_nan", [True, False])
+def test_fp8_linear_special_values(fm, with_nan):
+    """Non-finite and out-of-range activations: the e4m3 conversion saturates
+    +-inf and values past 448 to +-448, a NaN stays a NaN code (so its row of Y
+    is NaN), and max |X| is NaN if any element is, else +inf."""
+    M, K, N = 300, 256, 192
+    case(f"fp8_linear special values nan={with_nan}")
+    a = synth.attn_inputs(M=M, d=K, qkv=N, seed=77)
+    Xb = a["X"].copy()
+    specials = {(130, 3): np.inf, (131, 200): -np.inf, (250, 0): 1e30, (251, 9): -3e4}
+    if with_nan:
+        specials[(5, 17)] = np.nan
+    for (r, c), v in specials.items():
+        Xb[r, c] = synth.to_bf16_bits(np.array([v], dtype=np.float32))[0]
+    Wt, _, inv_w, _ = O.cast_transpose(a["Wqkv"])
+    sx = 0.5
+    X = bf16_dev(Xb)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    xam = f32_dev(-1.0)
+    fm.fp8_linear(X, f32_dev(sx), torch.from_numpy(Wt).to(DEV), f32_dev(inv_w), Y, xam)
+    torch.cuda.synchronize()
+    ref = F.bf16_to_f64(O.fp8_linear(Xb, sx, Wt, inv_w))
+    got = F.bf16_to_f64(bits(Y))
+    assert (np.isnan(got) == np.isnan(ref)).all()
+    fin = ~np.isnan(ref)
+    assert np.isfinite(got[fin]).all()
+    assert rel_fro(got[fin], ref[fin]) < 4e-3
+    if with_nan:
+        assert np.isnan(xam.item())
+    else:
+        assert xam.item() == np.inf
