@@ -323,7 +323,7 @@ const char* fp8mlp_status_str(int status) {
   switch (status) {
     case FP8MLP_OK: return "ok";
     case FP8MLP_E_NULL: return "a required pointer is NULL";
-    case FP8MLP_E_SHAPE: return "invalid size (negative, zero where not allowed, or not a multiple of 64)";
+    case FP8MLP_E_SHAPE: return "invalid size (negative, zero where not allowed, not a multiple of 64, or beyond the 32-bit addressing limits)";
     case FP8MLP_E_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FP8MLP_E_WORKSPACE: return "workspace missing or too small";
     case FP8MLP_E_ARCH: return "the current device is not gfx950 (MI355X)";

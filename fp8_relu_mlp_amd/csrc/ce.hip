@@ -335,7 +335,7 @@ static int ce_impl(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q,
                    const float* dloss, float* loss_out, float* lse_out, uint16_t* dX, float* dW, int accumulate,
                    int64_t M, int64_t V, int64_t d, void* workspace, size_t workspace_bytes, hipStream_t st) {
   FP8MLP_REQUIRE(M >= 0 && V > 0 && d > 0 && V % 64 == 0 && d % (FP8 ? 128 : 64) == 0 &&
-                     M * V < ((int64_t)1 << 40),
+                     M * V < ((int64_t)1 << 40) && weight_dims_ok(V, d),
                  FP8MLP_E_SHAPE);
   FP8MLP_REQUIRE(T >= 1 && T <= kCeMaxTargets, FP8MLP_E_ARG);
   FP8MLP_REQUIRE(softcap >= 0.0f && softcap <= 3.4e38f, FP8MLP_E_ARG);

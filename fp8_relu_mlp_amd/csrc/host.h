@@ -40,6 +40,23 @@ inline int launch_status() {
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The GEMMs address memory through buffer resources with 32-bit byte
+// offsets: from a tile's origin across its rows (up to 256 rows of a matrix
+// whose rows hold a feature size of elements), and across a whole weight
+// matrix where the weight is the row-contiguous operand.  Feature sizes up to
+// 2^22 and weights below 2^31 elements keep both inside 2^32 bytes.
+constexpr int64_t kMaxFeature = (int64_t)1 << 22;
+inline bool weight_dims_ok(int64_t rows, int64_t cols) {
+  return rows <= kMaxFeature && cols <= kMaxFeature && rows * cols < ((int64_t)1 << 31);
+}
+// Rows of a row-contiguous operand that one GEMM launch may address in a
+// single k range: rows of row_bytes bytes within 2^31 bytes, a multiple of
+// 64 (the split-k granule).
+inline int64_t max_k_range(int64_t row_bytes) {
+  const int64_t r = (((int64_t)1 << 31) / row_bytes) / 64 * 64;
+  return r > 64 ? r : 64;
+}
+
 #define FP8MLP_TRY(...)                  \
   do {                                   \
     int _st = (__VA_ARGS__);             \

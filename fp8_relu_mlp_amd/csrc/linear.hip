@@ -464,7 +464,7 @@ size_t fp8_linear_workspace(int64_t M, int64_t K) {
 int fp8_linear(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, const float* w_inv_scale,
                uint16_t* Y, float* x_amax_out, int64_t M, int64_t K, int64_t N, void* workspace,
                size_t workspace_bytes, void* stream) {
-  FP8MLP_REQUIRE(M >= 0 && K > 0 && N > 0 && K % 64 == 0 && N % 64 == 0, FP8MLP_E_SHAPE);
+  FP8MLP_REQUIRE(M >= 0 && K > 0 && N > 0 && K % 64 == 0 && N % 64 == 0 && weight_dims_ok(K, N), FP8MLP_E_SHAPE);
   FP8MLP_REQUIRE(x_scale && w_inv_scale && Wt_q, FP8MLP_E_NULL);
   // block 0 of the GEMM writes x_amax_out while its other blocks read the scales
   FP8MLP_REQUIRE(x_amax_out != x_scale && x_amax_out != w_inv_scale, FP8MLP_E_ARG);
@@ -487,7 +487,7 @@ int fp8_linear(const uint16_t* X, const float* x_scale, const uint8_t* Wt_q, con
   const int64_t Kp = lin_kp(K);
   uint8_t* Xq = (uint8_t*)workspace;
   uint32_t* xpart = (uint32_t*)((uint8_t*)workspace + align_up((size_t)(M * Kp), 256));
-  if (Kp <= lp::KMAX && K * N < (int64_t)1 << 32 && cdiv(M, lp::BM) * cdiv(N, lp::BN) < (int64_t)1 << 31) {
+  if (Kp <= lp::KMAX && cdiv(M, lp::BM) * cdiv(N, lp::BN) < (int64_t)1 << 31) {
     const int64_t tiles_m = cdiv(M, lp::BM), tiles_n = cdiv(N, lp::BN), items = tiles_m * tiles_n;
     const int64_t grid = items < num_cus() ? items : num_cus();
     PanelArgs pa{X, Wt_q, Y, x_scale, w_inv_scale, x_amax_out ? xpart : nullptr, M, K, N, (uint32_t)(K * N),

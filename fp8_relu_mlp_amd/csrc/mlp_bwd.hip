@@ -45,6 +45,9 @@ static BwdPlan bwd_plan(int64_t M, int64_t d, int64_t h) {
   if (s < 1) s = 1;
   p.k_per_split = cdiv(cdiv(M, s), 64) * 64;
   if (p.k_per_split == 0) p.k_per_split = 64;
+  // the dW GEMMs read one token range of dpre, X, dY and post per block
+  const int64_t kmax = max_k_range(2 * (d > h ? d : h));
+  if (p.k_per_split > kmax) p.k_per_split = kmax;
   p.splits = (int)(M > 0 ? cdiv(M, p.k_per_split) : 1);
   // the partials of dW1, then those of dW2, each split a whole number of
   // tiles (dW1 [h, d] and dW2 [d, h] have the same tile count)
@@ -236,7 +239,7 @@ static int mlp_bwd_impl(const uint16_t* dY, const uint16_t* X, const uint16_t* W
                         const void* post, const float* post_scale, uint16_t* dX, float* dW1, float* dW2,
                         int accumulate, int64_t M, int64_t d, int64_t h, void* workspace, size_t workspace_bytes,
                         hipStream_t st) {
-  FP8MLP_REQUIRE(M >= 0 && d > 0 && h > 0 && d % 64 == 0 && h % 64 == 0, FP8MLP_E_SHAPE);
+  FP8MLP_REQUIRE(M >= 0 && d > 0 && h > 0 && d % 64 == 0 && h % 64 == 0 && weight_dims_ok(h, d), FP8MLP_E_SHAPE);
   FP8MLP_REQUIRE(accumulate == 0 || accumulate == 1, FP8MLP_E_ARG);
   FP8MLP_REQUIRE(dW1 && dW2, FP8MLP_E_NULL);
   if (M > 0) FP8MLP_REQUIRE(dY && X && W1 && W2 && post && dX && (!Q || post_scale), FP8MLP_E_NULL);

@@ -45,7 +45,7 @@ static int fwd_check_args(int mode, const uint16_t* X, const uint16_t* W1, const
                           const uint16_t* Y, int64_t M, int64_t d, int64_t h) {
   const bool train = mode == FP8MLP_TRAIN_FP8;
   FP8MLP_REQUIRE(mode == FP8MLP_TRAIN_FP8 || mode == FP8MLP_EVAL_BF16, FP8MLP_E_ARG);
-  FP8MLP_REQUIRE(M >= 0 && d > 0 && h > 0 && d % 64 == 0 && h % 64 == 0, FP8MLP_E_SHAPE);
+  FP8MLP_REQUIRE(M >= 0 && d > 0 && h > 0 && d % 64 == 0 && h % 64 == 0 && weight_dims_ok(h, d), FP8MLP_E_SHAPE);
   FP8MLP_REQUIRE(!train || h % 128 == 0, FP8MLP_E_SHAPE);
   FP8MLP_REQUIRE(amax_out != nullptr, FP8MLP_E_NULL);
   if (M > 0) FP8MLP_REQUIRE(X && W1 && Y && (post || train), FP8MLP_E_NULL);
@@ -198,7 +198,7 @@ int mlp_relu2_fwd_fp8up(const uint16_t* X, const float* x_scale, const uint8_t* 
                         uint16_t* post, uint8_t* post_q, float* amax_out, float* scale_out, uint16_t* Y,
                         float* x_amax_out, int64_t M, int64_t d, int64_t h, void* workspace, size_t workspace_bytes,
                         void* stream) {
-  FP8MLP_REQUIRE(M >= 0 && d > 0 && h > 0 && d % 128 == 0 && h % 128 == 0, FP8MLP_E_SHAPE);
+  FP8MLP_REQUIRE(M >= 0 && d > 0 && h > 0 && d % 128 == 0 && h % 128 == 0 && weight_dims_ok(h, d), FP8MLP_E_SHAPE);
   FP8MLP_REQUIRE(x_scale && W1t_q && w1_inv_scale && W2t_q && w2_inv_scale && amax_prev && amax_out, FP8MLP_E_NULL);
   if (M > 0) FP8MLP_REQUIRE(X && post_q && Y, FP8MLP_E_NULL);
   FP8MLP_REQUIRE(margin > 0.0f && margin <= 3.4e38f, FP8MLP_E_ARG);

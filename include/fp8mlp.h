@@ -23,7 +23,10 @@
  *  - Every tensor pointer must be 16-byte aligned.  Feature sizes must be
  *    positive multiples of 64 (the contraction sizes of the e4m3 GEMMs,
  *    multiples of 128); the token count M may be any value >= 0 (ragged
- *    tails are masked, M = 0 is a valid empty call).
+ *    tails are masked, M = 0 is a valid empty call).  The GEMM entry points
+ *    also take feature sizes of at most 2^22 and weights of fewer than 2^31
+ *    elements (the kernels address memory with 32-bit byte offsets); larger
+ *    sizes return FP8MLP_E_SHAPE.
  *  - Scalars that change from step to step (amax, scales) live in device
  *    memory as fp32 so a training step never synchronises with the host.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
@@ -52,7 +55,7 @@ extern "C" {
 enum {
   FP8MLP_OK = 0,
   FP8MLP_E_NULL = -1,      /* a required pointer is NULL */
-  FP8MLP_E_SHAPE = -2,     /* a size is negative, zero where not allowed, or not a multiple of 64 */
+  FP8MLP_E_SHAPE = -2,     /* a size is negative, zero where not allowed, not a multiple of 64, or too large */
   FP8MLP_E_ALIGN = -3,     /* a tensor pointer is not 16-byte aligned */
   FP8MLP_E_WORKSPACE = -4, /* workspace missing or smaller than the *_workspace() size */
   FP8MLP_E_ARCH = -5,      /* the current device is not gfx950 */

@@ -97,6 +97,19 @@ def test_workspace_sizes(L):
     assert L.fp8_cast_transpose_workspace(768, 3072) >= 256
 
 
+def test_bwd_split_ranges_fit_32bit_offsets(L):
+    """The dW GEMMs address one token range of dpre / dY (rows of 2 max(d, h)
+    bytes) with 32-bit byte offsets: at 4M tokens the backward's workspace
+    must hold split-k partials for at least M * 2 max(d, h) / 2^31 ranges
+    (each split: one fp32 copy of dW1 and one of dW2)."""
+    d, h = 768, 3072
+    for M in (1 << 22, 3 << 21):
+        ws = L.mlp_relu2_bwd_workspace(M, d, h)
+        fixed = M * h * 2 + 2 * h * d * 2                  # dpre, W1t and W2t
+        min_splits = -(-M * 2 * max(d, h) // (1 << 31))
+        assert ws - fixed >= 2 * min_splits * h * d * 4, (M, ws)
+
+
 def _fwd(L, **kw):
     args = dict(mode=0, X=16, W1=16, W2t_q=16, w2_inv=16, W2=None, amax_prev=32, margin=2.0, post=16,
                 post_q=16, amax_out=48, scale_out=None, Y=16, M=256, d=128, h=512, ws=16, wsb=1 << 20,
@@ -111,6 +124,9 @@ def test_fwd_validation_before_any_device_call(L_nogpu):
     assert _fwd(L, d=100) == E_SHAPE
     assert _fwd(L, h=192) == E_SHAPE            # train needs h % 128 == 0
     assert _fwd(L, M=-1) == E_SHAPE
+    # past the 32-bit addressing limits: a feature size above 2^22, a weight of 2^31 elements
+    assert _fwd(L, d=(1 << 22) + 64) == E_SHAPE
+    assert _fwd(L, d=1 << 16, h=1 << 15) == E_SHAPE
     assert _fwd(L, X=None) == E_NULL
     assert _fwd(L, amax_out=None) == E_NULL
     assert _fwd(L, post_q=None) == E_NULL
@@ -142,6 +158,8 @@ def test_bwd_and_misc_validation(L_nogpu):
                                                  stream=None), **kw).values())
     assert b(acc=2) == E_ARG
     assert b(h=100) == E_SHAPE
+    assert b(h=(1 << 22) + 128) == E_SHAPE
+    assert b(d=1 << 15, h=1 << 16) == E_SHAPE
     assert b(dW1=None) == E_NULL
     assert b(post=40) == E_ALIGN
     assert b(wsb=10) == E_WS
@@ -157,11 +175,19 @@ def test_bwd_and_misc_validation(L_nogpu):
     lin = lambda **kw: L.fp8_linear(*dict(dict(X=16, xs=16, W=16, wi=16, Y=16, am=None, M=100, K=256, N=256,
                                                 ws=16, wsb=1 << 20, st=None), **kw).values())
     assert lin(K=160) == E_SHAPE              # K % 64
+    assert lin(N=(1 << 22) + 64) == E_SHAPE
+    assert lin(K=1 << 16, N=1 << 15) == E_SHAPE   # Wt_q of 2^31 codes
     assert lin(xs=None) == E_NULL
     assert lin(Y=17) == E_ALIGN
     assert lin(ws=None) == E_WS
     assert lin(wsb=100) == E_WS
     assert lin(am=16) == E_ARG                # x_amax_out aliases x_scale
+    # X, W, targets, T, weights, softcap, dloss, loss_out, lse_out, dX, dW, accumulate, M, V, d
+    ce = lambda M, V, d: L.softcap_ce_fwd_bwd(16, 16, 16, 1, 16, 15.0, None, 16, None, 16, 16, 0, M, V, d,
+                                              16, 1 << 40, None)
+    assert ce(256, 100, 64) == E_SHAPE        # V % 64
+    assert ce(256, (1 << 22) + 64, 64) == E_SHAPE
+    assert ce(256, 1 << 16, 1 << 15) == E_SHAPE   # W of 2^31 elements
 
 
 def test_stack_helpers_validation(L_nogpu):
@@ -192,6 +218,7 @@ def test_variant_entry_points_validation(L_nogpu):
     args = [16, 20, 16, 24, 16, 28, 32, 2.0, 16, 16, 36, 40, 16, 44]
     assert L.mlp_relu2_fwd_fp8up(*args, 256, 192, 256, 16, ws, None) == E_SHAPE    # d % 128
     assert L.mlp_relu2_fwd_fp8up(*args, 256, 128, 192, 16, ws, None) == E_SHAPE    # h % 128
+    assert L.mlp_relu2_fwd_fp8up(*args, 256, 1 << 16, 1 << 15, 16, ws, None) == E_SHAPE  # 2^31-element W1
     bad = list(args)
     bad[1] = None                                                                   # x_scale
     assert L.mlp_relu2_fwd_fp8up(*bad, 256, 128, 256, 16, ws, None) == E_NULL
