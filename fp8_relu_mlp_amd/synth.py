@@ -76,6 +76,42 @@ def mlp_inputs(M, d, h, seed, with_dy=False, step=0):
     return out
 
 
+def normal_f32_rows(shape, seed, name, blocks=16):
+    """float32 N(0, 1) draws for tensors of millions of rows, fast: the rows
+    split into ``blocks`` runs of equal length (the last one shorter), each
+    drawn in float32 from its own stream seeded with (seed, crc32(name),
+    block) on up to 8 threads.  The values do not depend on the threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    rows = shape[0]
+    out = np.empty(shape, dtype=np.float32)
+    per = -(-rows // blocks)
+
+    def fill(b):
+        g = np.random.default_rng([int(seed), zlib.crc32(name.encode()), b])
+        part = out[b * per:(b + 1) * per]
+        if part.size:
+            g.standard_normal(out=part, dtype=np.float32)
+
+    with ThreadPoolExecutor(8) as ex:
+        list(ex.map(fill, range(blocks)))
+    return out
+
+
+def normal_bf16_rows(shape, var, seed, name):
+    """bf16 bits of N(0, var) from ``normal_f32_rows`` (scaled in float32)."""
+    x = normal_f32_rows(shape, seed, name)
+    x *= np.float32(np.sqrt(var))
+    return to_bf16_bits(x)
+
+
+def abs_normal_bf16_rows(shape, seed, name):
+    """bf16 bits of |N(0, 1)| from ``normal_f32_rows``: a non-negative stand-in
+    for the stored activation when the backward is tested on its own."""
+    x = normal_f32_rows(shape, seed, name)
+    np.abs(x, out=x)
+    return to_bf16_bits(x)
+
+
 def perturbed_w1(W1_bits, seed):
     """Step-2 weights of the two-step forward workload: W1 + 1e-3 * N(0, 1/d),
     added in fp32 and rounded back to bf16 (a new input, not part of the path)."""

@@ -290,6 +290,54 @@ def test_bwd_ragged_mid_size(fm):
     assert rel_fro(dW2.cpu().numpy()[:, [5, h - 1]].astype(np.float64), bs["dW2_cols"]) < 1e-4
 
 
+@pytest.mark.timeout(300)
+def test_bwd_token_ranges_past_32bit_offsets(fm):
+    """M = 1474560 tokens (30 x 49152) at d=768, h=3072, the backward alone.
+    Rows of dpre and post hold 6144 bytes, so the dW GEMMs take the tokens in
+    ranges of at most 349504 (2^31 bytes of a row-contiguous operand per
+    range, addressed with 32-bit offsets): five ranges here, the last one
+    ragged; one range of all tokens would span 9 GB.  Rows of dW1 and
+    columns of dW2 (sums over every token) and rows of dX against the oracle.
+    post is a synthetic non-negative input (|N(0,1)|).  The sampled dW
+    entries come from the oracle's sampled backward restricted to the hidden
+    units they involve (hidden unit i's dpre column depends only on post
+    column i and W2 column i)."""
+    M, d, h = 30 * 49152, 768, 3072
+    seed = 11
+    case(f"backward over several token ranges: drawing inputs M={M} d={d} h={h}")
+    X = synth.normal_bf16_rows((M, d), 1.0, seed, "X")
+    dY = synth.normal_bf16_rows((M, d), 1e-3, seed, "dY")
+    post = synth.abs_normal_bf16_rows((M, h), seed, "post")
+    W1 = synth.normal_bf16((h, d), 1.0 / d, seed, "W1")
+    W2 = synth.normal_bf16((d, h), 1.0 / h, seed, "W2")
+    case(f"backward over several token ranges M={M} d={d} h={h}")
+    Xd, dYd, postd = bf16_dev(X), bf16_dev(dY), bf16_dev(post)
+    dX = torch.empty_like(Xd)
+    dW1 = torch.empty((h, d), dtype=torch.float32, device=DEV)
+    dW2 = torch.empty((d, h), dtype=torch.float32, device=DEV)
+    fm.mlp_relu2_bwd(dYd, Xd, bf16_dev(W1), bf16_dev(W2), postd, dX, dW1, dW2)
+    torch.cuda.synchronize()
+    del postd
+    bounds = [k * 349504 for k in range(1, 5)]
+    rows = np.array(sorted({0, M - 1, *bounds, *(b - 1 for b in bounds), 123457, 1400001}))
+    r1, c2 = [0, 1234, h - 1], [0, 777, h - 1]
+    dx = F.bf16_to_f64(bits(dX)[rows])
+    dw1 = dW1.cpu().numpy()[r1].astype(np.float64)
+    dw2 = dW2.cpu().numpy()[:, c2].astype(np.float64)
+    case("backward over several token ranges: oracle on sampled outputs")
+    ref_rows = O.mlp_bwd_sampled(dY[rows], X[rows], W1, W2, F.bf16_to_f64(post[rows]), np.arange(len(rows)), [], [])
+    units = r1 + c2
+    ref_w = O.mlp_bwd_sampled(dY, X, W1[units], W2[:, units], F.bf16_to_f64(post[:, units]), [], [0, 1, 2],
+                              [3, 4, 5])
+    assert rel_fro(dx, ref_rows["dX_rows"]) < 4e-3
+    assert rel_fro(dw1, ref_w["dW1_rows"]) < 4e-3
+    assert rel_fro(dw2, ref_w["dW2_cols"]) < 1e-4
+    for k in range(3):
+        # every sampled gradient row / column on its own, not only in aggregate
+        assert rel_fro(dw1[k], ref_w["dW1_rows"][k]) < 1e-2, r1[k]
+        assert rel_fro(dw2[:, k], ref_w["dW2_cols"][:, k]) < 1e-4, c2[k]
+
+
 def test_fp8up_full_size_sampled(fm):
     """The e4m3 up-projection forward at the timed workload's size
     (M=49152, d=768, h=3072) through Relu2MLP(fp8_up=True): amaxes
