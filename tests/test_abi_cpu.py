@@ -99,11 +99,12 @@ def test_workspace_sizes(L):
 
 def test_bwd_split_ranges_fit_32bit_offsets(L):
     """The dW GEMMs address one token range of dpre / dY (rows of 2 max(d, h)
-    bytes) with 32-bit byte offsets: at 4M tokens the backward's workspace
-    must hold split-k partials for at least M * 2 max(d, h) / 2^31 ranges
-    (each split: one fp32 copy of dW1 and one of dW2)."""
-    d, h = 768, 3072
-    for M in (1 << 22, 3 << 21):
+    bytes) with 32-bit byte offsets: the backward's workspace must hold
+    split-k partials for at least M * 2 max(d, h) / 2^31 ranges (each split:
+    one fp32 copy of dW1 and one of dW2), at 4M and 6M tokens of the
+    GPT-2-small block and at 300000 tokens of a d=2048, h=8192 block, whose
+    256 dW tiles alone would leave the tokens in one range."""
+    for M, d, h in ((1 << 22, 768, 3072), (3 << 21, 768, 3072), (300000, 2048, 8192)):
         ws = L.mlp_relu2_bwd_workspace(M, d, h)
         fixed = M * h * 2 + 2 * h * d * 2                  # dpre, W1t and W2t
         min_splits = -(-M * 2 * max(d, h) // (1 << 31))

@@ -292,17 +292,18 @@ def test_bwd_ragged_mid_size(fm):
 
 @pytest.mark.timeout(300)
 def test_bwd_token_ranges_past_32bit_offsets(fm):
-    """M = 1474560 tokens (30 x 49152) at d=768, h=3072, the backward alone.
-    Rows of dpre and post hold 6144 bytes, so the dW GEMMs take the tokens in
-    ranges of at most 349504 (2^31 bytes of a row-contiguous operand per
-    range, addressed with 32-bit offsets): five ranges here, the last one
-    ragged; one range of all tokens would span 9 GB.  Rows of dW1 and
-    columns of dW2 (sums over every token) and rows of dX against the oracle.
-    post is a synthetic non-negative input (|N(0,1)|).  The sampled dW
-    entries come from the oracle's sampled backward restricted to the hidden
-    units they involve (hidden unit i's dpre column depends only on post
-    column i and W2 column i)."""
-    M, d, h = 30 * 49152, 768, 3072
+    """The backward of a wider block, d=2048, h=8192, at M = 300000 tokens.
+    dW has 256 tiles here, enough blocks without splitting the tokens, but
+    rows of dpre and post hold 16384 bytes: the dW GEMMs address one token
+    range per block with 32-bit offsets, so the tokens go in ranges of at
+    most 131072 (2^31 bytes of a row-contiguous operand): three ranges, the
+    last ragged (37856 tokens), where one range of all tokens would span
+    4.9 GB.  Rows of dW1 and columns of dW2 (sums over every token) and rows
+    of dX against the oracle.  post is a synthetic non-negative input
+    (|N(0,1)|).  The sampled dW entries come from the oracle's sampled
+    backward restricted to the hidden units they involve (hidden unit i's
+    dpre column depends only on post column i and W2 column i)."""
+    M, d, h = 300000, 2048, 8192
     seed = 11
     case(f"backward over several token ranges: drawing inputs M={M} d={d} h={h}")
     X = synth.normal_bf16_rows((M, d), 1.0, seed, "X")
@@ -318,9 +319,9 @@ def test_bwd_token_ranges_past_32bit_offsets(fm):
     fm.mlp_relu2_bwd(dYd, Xd, bf16_dev(W1), bf16_dev(W2), postd, dX, dW1, dW2)
     torch.cuda.synchronize()
     del postd
-    bounds = [k * 349504 for k in range(1, 5)]
-    rows = np.array(sorted({0, M - 1, *bounds, *(b - 1 for b in bounds), 123457, 1400001}))
-    r1, c2 = [0, 1234, h - 1], [0, 777, h - 1]
+    bounds = [131072, 262144]
+    rows = np.array(sorted({0, M - 1, *bounds, *(b - 1 for b in bounds), 12345, 200001}))
+    r1, c2 = [0, 5000, h - 1], [0, 777, h - 1]
     dx = F.bf16_to_f64(bits(dX)[rows])
     dw1 = dW1.cpu().numpy()[r1].astype(np.float64)
     dw2 = dW2.cpu().numpy()[:, c2].astype(np.float64)
