@@ -89,7 +89,7 @@ def test_mlp_fwd_bwd_stay_inside(fm, M, d, h):
     assert torch.isfinite(dW1).all() and torch.isfinite(Y.float()).all()
 
 
-@pytest.mark.parametrize("M,K,N", [(1000, 256, 320), (333, 768, 2304), (700, 192, 256)])
+@pytest.mark.parametrize("M,K,N", [(1000, 256, 320), (333, 768, 2304), (700, 192, 256), (601, 960, 320)])
 def test_fp8_linear_stays_inside(fm, M, K, N):
     case(f"guard bands fp8_linear M={M} K={K} N={N}")
     L = fm.lib()

@@ -52,10 +52,11 @@ def run_linear(fm, Xb, Wb, margin=1.0, scale_in=None):
 # 768 runs the row-panel kernel: (8192, 768, 2304) and (40000, 128, 512) give
 # its blocks several output tiles each, with changes of row panel inside a
 # block (the second with two 64-k tiles per output tile); (3000, 768, 320)
-# has a part-filled last column tile.  K = 1024 runs the two-launch path.
+# has a part-filled last column tile.  K = 1024 runs the two-launch path,
+# K = 960 the same with e4m3 rows padded to 1024 codes.
 @pytest.mark.parametrize("M,K,N", [(1000, 768, 2304), (777, 768, 768), (1, 128, 64), (300, 256, 192),
                                    (513, 64, 128), (1000, 320, 576), (8192, 768, 2304), (40000, 128, 512),
-                                   (3000, 768, 320), (600, 1024, 256)])
+                                   (3000, 768, 320), (600, 1024, 256), (400, 960, 192)])
 def test_fp8_linear_parity(fm, M, K, N):
     case(f"fp8_linear M={M} K={K} N={N}")
     a = synth.attn_inputs(M=M, d=K, qkv=N, seed=90 + M)
