@@ -104,6 +104,22 @@ def test_fp8post_ragged_shapes(fm, M, d, h):
     check(ins, out, b)
 
 
+def _sweep_shapes():
+    """Six seeded shapes: M in 1..3000, d a multiple of 64 up to 1536, h a
+    multiple of 128 up to 3072."""
+    rng = np.random.default_rng(2028)
+    return [(int(rng.integers(1, 3001)), 64 * int(rng.integers(1, 25)), 128 * int(rng.integers(1, 25)))
+            for _ in range(6)]
+
+
+@pytest.mark.parametrize("M,d,h", _sweep_shapes())
+def test_fp8post_shape_sweep(fm, M, d, h):
+    case(f"fp8post shape sweep M={M} d={d} h={h}")
+    ins = synth.mlp_inputs(M, d, h, 7000 + M, with_dy=True)
+    out, b = run(fm, ins)
+    check(ins, out, b)
+
+
 def test_fp8post_saturating_scale(fm):
     """amax_prev far below this step's amax: the e4m3 copy clips, and the
     backward still matches the oracle run on the same codes."""

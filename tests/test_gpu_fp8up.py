@@ -149,6 +149,23 @@ def test_fp8up_ragged_shapes(fm, M, d, h):
     check(ins, g, sx, 3.0)
 
 
+def _sweep_shapes():
+    """Six seeded shapes: M in 1..3000, d and h multiples of 128 (the e4m3
+    contractions) up to 1536 and 3072."""
+    rng = np.random.default_rng(2027)
+    return [(int(rng.integers(1, 3001)), 128 * int(rng.integers(1, 13)), 128 * int(rng.integers(1, 25)))
+            for _ in range(6)]
+
+
+@pytest.mark.parametrize("M,d,h", _sweep_shapes())
+def test_fp8up_shape_sweep(fm, M, d, h):
+    case(f"fp8up shape sweep M={M} d={d} h={h}")
+    ins = synth.mlp_inputs(M, d, h, 6000 + M)
+    sx = O.delayed_scale(O.amax(F.bf16_to_f64(ins["X"])), 2.0)
+    g = run(fm, ins, sx, 2.5)
+    check(ins, g, sx, 2.5)
+
+
 def test_fp8up_lossless_special_case(fm):
     """X, W1 in {-1,0,1} (<= 3 non-zeros per W1 row), W2 in {-1,0,1}, the X
     and weight scales 1, amax_prev 7, margin 2: every quantisation is exact,

@@ -77,6 +77,29 @@ def test_fp8_linear_parity(fm, M, K, N):
     assert rel_fro(Y, exact) < 0.08
 
 
+def _sweep_shapes():
+    """Eight seeded shapes: M in 1..20000, K a multiple of 64 up to 1536 (the
+    row-panel kernel up to 768, the two-launch path above), N a multiple of
+    64 up to 3072."""
+    rng = np.random.default_rng(2029)
+    return [(int(rng.integers(1, 20001)), 64 * int(rng.integers(1, 25)), 64 * int(rng.integers(1, 49)))
+            for _ in range(8)]
+
+
+@pytest.mark.parametrize("M,K,N", _sweep_shapes())
+def test_fp8_linear_shape_sweep(fm, M, K, N):
+    case(f"fp8_linear shape sweep M={M} K={K} N={N}")
+    a = synth.attn_inputs(M=M, d=K, qkv=N, seed=8000 + M)
+    g = run_linear(fm, a["X"], a["Wqkv"])
+    Xf = F.bf16_to_f64(a["X"])
+    assert f32_bits(g["xamax"]) == f32_bits(O.amax(Xf))
+    sx = O.exact_scale(O.amax(Xf))
+    Wt, _, inv_w, _ = O.cast_transpose(a["Wqkv"])
+    assert (Wt == g["Wt"]).all()
+    ref = F.bf16_to_f64(O.fp8_linear(a["X"], sx, Wt, inv_w))
+    assert rel_fro(F.bf16_to_f64(g["Y"]), ref) < 4e-3
+
+
 @pytest.mark.parametrize("K", [256, 192])
 def test_fp8_linear_lossless(fm, K):
     M, N = 500, 128

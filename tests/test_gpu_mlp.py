@@ -228,6 +228,31 @@ def test_bwd_parity(fm, M, d, h):
     assert rel_fro(dW1, ref["dW1"]) < 4e-3
 
 
+def _sweep_shapes():
+    """Ten seeded shapes: M in 1..3000, d a multiple of 64 up to 1536, h a
+    multiple of 128 up to 3072 (ragged in every dimension against the
+    256-, 192- and 384-wide tiles)."""
+    rng = np.random.default_rng(2026)
+    return [(int(rng.integers(1, 3001)), 64 * int(rng.integers(1, 25)), 128 * int(rng.integers(1, 25)))
+            for _ in range(10)]
+
+
+@pytest.mark.parametrize("M,d,h", _sweep_shapes())
+def test_fwd_bwd_shape_sweep(fm, M, d, h):
+    """Forward gates and the backward against the oracle's whole tensors, on
+    seeded shapes none of the hand-picked cases use."""
+    ins = synth.mlp_inputs(M, d, h, 5000 + M, with_dy=True)
+    case(f"shape sweep fwd M={M} d={d} h={h}")
+    g = run_fwd(fm, ins, amax_prev=2.5)
+    check_fwd_gates(ins, g, 2.5)
+    case(f"shape sweep bwd M={M} d={d} h={h}")
+    dX, dW1, dW2 = run_bwd(fm, ins, g["post"])
+    ref = O.mlp_bwd(ins["dY"], ins["X"], ins["W1"], ins["W2"], F.bf16_to_f64(g["post"]))
+    assert rel_fro(F.bf16_to_f64(dX), ref["dX"]) < 4e-3
+    assert rel_fro(dW1, ref["dW1"]) < 4e-3
+    assert rel_fro(dW2, ref["dW2"]) < 1e-4
+
+
 def test_bwd_accumulate_and_empty(fm):
     M, d, h = 700, 128, 256
     ins = synth.mlp_inputs(M, d, h, 70, with_dy=True)
