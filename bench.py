@@ -156,9 +156,53 @@ def summarize_linear(outdir):
         roof = max(fl / (PEAK_FP8 * 1e12), by / (PEAK_HBM * 1e9)) * 1e6
         lines.append(f"| {proj} | {n} | fp8_linear_panel | {len(durs)} | {avg:.1f} | {fl / avg / 1e6:.0f} | "
                      f"{fl / avg / 1e6 / PEAK_FP8:.3f} | {by / avg / 1e3:.0f} | {roof / avg:.3f} |")
+    # counters (optional runs): HBM bytes scaled by the plain-copy calibration, matrix-core busy share
+    subs = [f"lin_{p}_{c}" for p in ("qkv", "o") for c in ("fetch", "write", "mfma")] + ["cfetch", "cwrite"]
+    if all(os.path.isdir(os.path.join(outdir, sub)) for sub in subs):
+        ff, _ = copy_calibration(outdir, "cfetch", "FETCH_SIZE")
+        wf, _ = copy_calibration(outdir, "cwrite", "WRITE_SIZE")
+        pmc = "rocprofv3 --pmc {c} --output-format csv -d OUT/lin_{p}_{s} -o k -- python3 bench.py --linear {p}"
+        lines += ["", "Counters per launch, one run per counter set and projection:", ""]
+        for s_, c in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE"), ("mfma", "MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_F8")):
+            lines.append("    " + pmc.format(c=c, p="{qkv,o}", s=s_))
+        lines += ["", f"HBM bytes: fetched = {ff:.3f} x FETCH_SIZE, written = {wf:.3f} x WRITE_SIZE (a plain 1 GiB",
+                  "device copy under the same counters, `bench.py --copy-calibration`).  `MfmaUtil`: busy cycles of",
+                  "the matrix cores over all SIMDs / (GPU active cycles x SIMDs), in per cent.", "",
+                  "| projection | fetched MB | written MB | total MB | algorithmic MB | total / algorithmic | "
+                  "MFMA GFLOP | MfmaUtil % |", "|---|---:|---:|---:|---:|---:|---:|---:|"]
+        for proj, n in (("qkv", 3 * D), ("o", D)):
+            def counter(sub, name):
+                vals = [float(r["Counter_Value"]) for r in csv_rows(outdir, f"lin_{proj}_{sub}", "*counter_collection.csv")
+                        if r["Counter_Name"] == name and logical_kernel_name(r["Kernel_Name"]) == "fp8_linear_panel"]
+                if not vals:
+                    raise SystemExit(f"no {name} of fp8_linear_panel under lin_{proj}_{sub}")
+                return sum(vals) / len(vals)
+            fb, wb = ff * 1024.0 * counter("fetch", "FETCH_SIZE"), wf * 1024.0 * counter("write", "WRITE_SIZE")
+            gf = 512.0 * counter("mfma", "SQ_INSTS_VALU_MFMA_MOPS_F8") / 1e9
+            _, by = linear_work(M, D, n)
+            lines.append(f"| {proj} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {(fb + wb) / 1e6:.1f} | {by / 1e6:.1f} | "
+                         f"{(fb + wb) / by:.2f} | {gf:.1f} | {counter('mfma', 'MfmaUtil'):.1f} |")
     with open(os.path.join(PROFILES, "kernel_trace_fp8_linear_M49152.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(f"wrote {PROFILES}/kernel_trace_fp8_linear_M49152.md")
+
+
+def csv_rows(outdir, sub, pattern):
+    """Rows of the first rocprofv3 CSV matching pattern under outdir/sub."""
+    files = sorted(glob.glob(os.path.join(outdir, sub, "**", pattern), recursive=True))
+    if not files:
+        raise SystemExit(f"no {pattern} under {os.path.join(outdir, sub)}")
+    with open(files[0]) as fh:
+        return list(csv.DictReader(fh))
+
+
+def copy_calibration(outdir, sub, counter, true_bytes=1 << 30):
+    """(bytes per counted unit, raw bytes) from the plain 1 GiB device copy's counter run under outdir/sub."""
+    vals = [float(r["Counter_Value"]) * 1024.0 for r in csv_rows(outdir, sub, "*counter_collection.csv")
+            if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no copy dispatch in {sub}")
+    return true_bytes / (sum(vals) / len(vals)), sum(vals) / len(vals)
 
 
 def summarize_profiles(outdir):
@@ -167,11 +211,7 @@ def summarize_profiles(outdir):
     cwrite/: the same counters for a plain 1 GiB device copy) into the text
     summaries under profiles/."""
     def rows(sub, pattern):
-        files = sorted(glob.glob(os.path.join(outdir, sub, "**", pattern), recursive=True))
-        if not files:
-            raise SystemExit(f"no {pattern} under {os.path.join(outdir, sub)}")
-        with open(files[0]) as fh:
-            return list(csv.DictReader(fh))
+        return csv_rows(outdir, sub, pattern)
 
     cmd_bench = "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-extras --no-graph"
     # kernel trace: per-dispatch durations
@@ -202,15 +242,8 @@ def summarize_profiles(outdir):
             acc.setdefault(logical_kernel_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]) * 1024.0)
         return {k: sum(v) / len(v) for k, v in acc.items()}
 
-    def copy_factor(sub, counter, true_bytes=1 << 30):
-        vals = [float(r["Counter_Value"]) * 1024.0 for r in rows(sub, "*counter_collection.csv")
-                if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
-        if not vals:
-            raise SystemExit(f"no copy dispatch in {sub}")
-        return true_bytes / (sum(vals) / len(vals)), sum(vals) / len(vals)
-
-    ff, fraw = copy_factor("cfetch", "FETCH_SIZE")
-    wf, wraw = copy_factor("cwrite", "WRITE_SIZE")
+    ff, fraw = copy_calibration(outdir, "cfetch", "FETCH_SIZE")
+    wf, wraw = copy_calibration(outdir, "cwrite", "WRITE_SIZE")
     fetch, write = per_kernel("fetch", "FETCH_SIZE"), per_kernel("write", "WRITE_SIZE")
     work = kernel_work(M, D, H)
     table = {}
