@@ -411,7 +411,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the FP8-linear / eval / ablation lines")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay pass (profiler runs)")
@@ -535,6 +535,29 @@ def main():
 
     blk.forward(X, post=post, post_q=post_q, Y=Y, workspace=ws_f)   # bootstrap amax_prev
     torch.cuda.synchronize()
+
+    # matrix-core rate on the workload's own operands (the clock under a dense
+    # MFMA load depends on the data; the published peaks assume 2.4 GHz).  It
+    # runs before the warm-up: its ~20 ms of dense matrix work bring the chip
+    # to the clocks it holds under this load, which an idle chip takes some
+    # 20 steps to reach (those steps run up to 10 % slower).
+    log("matrix-core rate probe")
+    sink = torch.empty(fm.PROBE_BLOCKS * 256, dtype=torch.float32, device=dev)
+
+    def probe_rate(dtype, a, b, iters=20000):
+        fm.mfma_probe(dtype, a, b, iters // 10, sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fl = fm.mfma_probe(dtype, a, b, iters, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        return fl / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+    probe = {"bf16_tflops": round(probe_rate(fm.MFMA_BF16, X, W1), 1),
+             "e4m3_tflops": round(probe_rate(fm.MFMA_E4M3, post_q, blk.W2t_q), 1),
+             "operands": "X and W1 (bf16), post_q and W2t_q (e4m3) of this workload"}
+
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
@@ -593,24 +616,6 @@ def main():
         graph_ms = graph_replay_ms(torch, step, args.steps)
         log(f"graph replay: {graph_ms:.3f} ms/step")
 
-    # matrix-core rate on the workload's own operands (the clock under a dense
-    # MFMA load depends on the data; the published peaks assume 2.4 GHz)
-    log("matrix-core rate probe")
-    sink = torch.empty(fm.PROBE_BLOCKS * 256, dtype=torch.float32, device=dev)
-
-    def probe_rate(dtype, a, b, iters=20000):
-        fm.mfma_probe(dtype, a, b, iters // 10, sink)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        fl = fm.mfma_probe(dtype, a, b, iters, sink)
-        e1.record()
-        torch.cuda.synchronize()
-        return fl / (e0.elapsed_time(e1) * 1e-3) / 1e12
-
-    probe = {"bf16_tflops": round(probe_rate(fm.MFMA_BF16, X, W1), 1),
-             "e4m3_tflops": round(probe_rate(fm.MFMA_E4M3, post_q, blk.W2t_q), 1),
-             "operands": "X and W1 (bf16), post_q and W2t_q (e4m3) of this workload"}
     roofline["probe_peak"] = probe["bf16_tflops"] if peak == PEAK_BF16 else probe["e4m3_tflops"]
     roofline["frac_of_probe_peak"] = round(achieved / roofline["probe_peak"], 4)
 
