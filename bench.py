@@ -128,6 +128,9 @@ def linear_work(M, d, n):
     return 2.0 * M * d * n, M * d * 2 + d * n + M * n * 2
 
 
+LIN_CALLS, LIN_KEPT = 40, 20   # fp8_linear calls per `--linear` run; the last ones summarised
+
+
 def summarize_linear(outdir):
     """profiles/kernel_trace_fp8_linear_M49152.md from rocprofv3 kernel traces of `bench.py --linear qkv`
     and `--linear o` under outdir/lin_qkv and outdir/lin_o."""
@@ -135,8 +138,9 @@ def summarize_linear(outdir):
     lines = ["# fp8_linear kernel durations: the QKV and output projections, M=49152, K=768 (one MI355X)", "",
              "Commands (from a scratch directory, TMPDIR=/tmp):", "", "    " + cmd.format(p="qkv"),
              "    " + cmd.format(p="o"), "",
-             "Summarised with `python3 bench.py --summarize-linear OUT`.  Seven calls per run (the first two",
-             "are warm-up, left out below).  Algorithmic bytes: X read once in bf16, the e4m3 weight, Y written",
+             f"Summarised with `python3 bench.py --summarize-linear OUT`.  Each run first runs the matrix-core",
+             f"probe (~20 ms of e4m3 MFMA work, so the chip holds its loaded clocks), then {LIN_CALLS} calls; the",
+             f"last {LIN_KEPT} are summarised.  Algorithmic bytes: X read once in bf16, the e4m3 weight, Y written",
              "in bf16.  Roofline time = max(flops / 5.0 PFLOP/s, bytes / 8 TB/s); fraction = roofline time /",
              "measured time.", "",
              "| projection | N | kernel | calls | avg us | TFLOP/s | of fp8 peak | GB/s alg. | of roofline |",
@@ -148,7 +152,7 @@ def summarize_linear(outdir):
         with open(files[0]) as fh:
             trace = list(csv.DictReader(fh))
         durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
-                if logical_kernel_name(r["Kernel_Name"]) == "fp8_linear_panel"][2:]
+                if logical_kernel_name(r["Kernel_Name"]) == "fp8_linear_panel"][-LIN_KEPT:]
         if not durs:
             raise SystemExit(f"no fp8_linear_panel dispatch in {files[0]}")
         avg = sum(durs) / len(durs)
@@ -504,10 +508,13 @@ def main():
         fm.fp8_scale_from_amax(amax, 1.0, sx)
         Ya = torch.empty((Xa.shape[0], n), dtype=torch.bfloat16, device=dev)
         wsl = torch.empty(max(1, fm.lib().fp8_linear_workspace(Xa.shape[0], D)), dtype=torch.uint8, device=dev)
-        for _ in range(7):
+        # the chip to the clocks it holds under matrix work first (as before the step's warm-up)
+        sink = torch.empty(fm.PROBE_BLOCKS * 256, dtype=torch.float32, device=dev)
+        fm.mfma_probe(fm.MFMA_E4M3, Wt, Wt, 20000, sink)
+        for _ in range(LIN_CALLS):
             fm.fp8_linear(Xa, sx, Wt, inv_w, Ya, workspace=wsl)
         torch.cuda.synchronize()
-        print(json.dumps({"projection": args.linear, "M": int(Xa.shape[0]), "K": D, "N": n, "calls": 7}))
+        print(json.dumps({"projection": args.linear, "M": int(Xa.shape[0]), "K": D, "N": n, "calls": LIN_CALLS}))
         return
     log("generating inputs")
     ins = synth.mlp_inputs(M, D, H, synth.WORKLOADS["fwdbwd"][3], with_dy=True)
