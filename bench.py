@@ -419,6 +419,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the FP8-linear / eval / ablation lines")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay pass (profiler runs)")
+    ap.add_argument("--sustain", type=float, metavar="SECONDS",
+                    help="after the warm-up, run the step back to back for SECONDS and print the rate only")
     ap.add_argument("--jsonl", metavar="PATH",
                     help="also append the record, with host cores, GPU identity and clocks, to this JSONL file")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -569,6 +571,18 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    if args.sustain:
+        # the warm step back to back for a while (for sampling the socket power beside it)
+        t0, n = time.time(), 0
+        while time.time() - t0 < args.sustain:
+            for _ in range(50):
+                step()
+            n += 50
+            torch.cuda.synchronize()
+        dt = time.time() - t0
+        print(json.dumps({"sustain_s": round(dt, 2), "steps": n, "us_per_step": round(1e6 * dt / n, 1)}))
+        return
 
     log(f"timing {args.steps} steps")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
