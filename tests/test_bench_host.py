@@ -2,8 +2,8 @@
 published-peak floor, the kernel-name mapping of rocprofv3 traces, the
 counter summaries and the one-GPU guard.
 
-The expected figures are the survey's hand-computed ones for this workload
-(M=49152, d=768, h=3072): per-kernel HBM bytes 533.2 / 228.9 / 684.2 /
+The expected figures are computed by hand for this workload (M=49152,
+d=768, h=3072): per-kernel HBM bytes 533.2 / 228.9 / 684.2 /
 386.9 / 386.9 / 382.2 MB, 1.3916 TFLOP per fwd+bwd, the mixed floor 506.9 us
 at 256 CU x 2.4 GHz peaks; fp8_linear QKV 173.9 GFLOP and 303.8 MB, O 58.0
 GFLOP and 151.6 MB.
@@ -41,8 +41,8 @@ def test_step_work_matches_the_hand_computed_table():
 
 
 def test_mixed_floor(monkeypatch):
-    # at the survey's 256 CU x 2.4 GHz peaks the floor is 506.9 us; at the
-    # rounded published 2.5 / 5.0 PFLOP/s it is 510.2 us
+    # at peaks from 256 CU x 2.4 GHz (2516.6 / 5033.2 TFLOP/s) the floor is
+    # 506.9 us; at the rounded published 2.5 / 5.0 PFLOP/s it is 510.2 us
     monkeypatch.setattr(bench, "PEAK_BF16", 2516.6)
     monkeypatch.setattr(bench, "PEAK_FP8", 5033.2)
     assert bench.mixed_floor_us(M, D, H) == pytest.approx(506.9, abs=0.05)
