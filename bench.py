@@ -640,6 +640,10 @@ def main():
     roofline["probe_peak"] = probe["bf16_tflops"] if peak == PEAK_BF16 else probe["e4m3_tflops"]
     roofline["frac_of_probe_peak"] = round(achieved / roofline["probe_peak"], 4)
 
+    power = None
+    if not args.no_extras:
+        log("socket power while the step runs back to back")
+        power = socket_power(torch, step)
     extras = {}
     if not args.no_extras:
         log("extra measurements")
@@ -673,6 +677,7 @@ def main():
         "mixed_mfma_floor_us": round(floor_us, 1),
         "roofline": roofline,
         "mfma_probe": probe,
+        "power": power,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "extras": extras,
@@ -712,6 +717,48 @@ def gpu_info(torch):
         except OSError:
             continue
     return info
+
+
+def socket_power(torch, step, seconds=3.0):
+    """Median socket power (amd-smi) while the step runs back to back for
+    `seconds`, sampled from a thread after the first second; None when
+    amd-smi is not there or reports nothing."""
+    import shutil
+    import subprocess
+    import threading
+    if shutil.which("amd-smi") is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sample():
+        t0 = time.time()
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "--power"], capture_output=True, text=True, timeout=10)
+                m = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", r.stdout)
+                if m and time.time() - t0 > 1.0:
+                    samples.append(float(m.group(1)))
+            except (OSError, subprocess.SubprocessError):
+                return
+            time.sleep(0.25)
+
+    th = threading.Thread(target=sample, daemon=True)
+    t0, n = time.time(), 0
+    th.start()
+    while time.time() - t0 < seconds:
+        for _ in range(20):
+            step()
+        n += 20
+        torch.cuda.synchronize()
+    dt = time.time() - t0
+    stop.set()
+    th.join(timeout=15)
+    if not samples:
+        return None
+    samples.sort()
+    return {"socket_w_median": samples[len(samples) // 2], "socket_w_max": samples[-1], "samples": len(samples),
+            "us_per_step": round(1e6 * dt / n, 1),
+            "how": f"amd-smi metric --power every ~0.3 s while the step ran back to back for {seconds:.0f} s"}
 
 
 def graph_replay_ms(torch, step, steps):
