@@ -96,3 +96,81 @@ def test_step_captured_in_a_graph_replays_like_eager():
         for k, v in eager[i].items():
             assert np.array_equal(got[k], v), (i, k)
         _ = float(amax_out.sum().item())                     # eager work between replays
+
+
+def test_linear_and_cross_entropy_captured_in_a_graph():
+    """fp8_linear on both of its paths (the row-panel kernel at K = 768, the
+    conversion pass and GEMM at K = 1024; max |X| from the per-block maxima)
+    and the softcapped cross-entropy in bf16 and with the e4m3 head, captured
+    once and replayed three times on new inputs written eagerly between the
+    replays: every replay equals the eager calls bit for bit."""
+    fm.lib()
+    L = fm.lib()
+    f = lambda v=0.0: torch.full((1,), v, dtype=torch.float32, device=DEV)
+    M = 1500
+    lin = []
+    for K, N in ((768, 2304), (1024, 320)):
+        a = synth.attn_inputs(M=M, d=K, qkv=N, seed=96 + K)
+        W = bf16_dev(a["Wqkv"])
+        Wt, inv = torch.empty((K, N), dtype=torch.uint8, device=DEV), f()
+        fm.fp8_cast_transpose(W, Wt, inv_scale_out=inv)
+        lin.append({"X": bf16_dev(a["X"]), "Wt": Wt, "inv": inv, "sx": f(8.0), "Y": torch.empty((M, N),
+                    dtype=torch.bfloat16, device=DEV), "xam": f(),
+                    "ws": torch.empty(max(1, L.fp8_linear_workspace(M, K)), dtype=torch.uint8, device=DEV)})
+    Mc, dc, V, T = 700, 256, 2048, 3
+    ci = synth.ce_inputs(Mc, dc, V, T, 97, seq=100, head_var=16.0)
+    Xc, Wc = bf16_dev(ci["X"]), bf16_dev(ci["W"])
+    tg = torch.from_numpy(ci["targets"].astype(np.int32)).to(DEV)
+    wts = torch.tensor([1.0, 0.5, 0.25], dtype=torch.float32, device=DEV)
+    Wct, cinv = torch.empty((dc, V), dtype=torch.uint8, device=DEV), f()
+    fm.fp8_cast_transpose(Wc, Wct, inv_scale_out=cinv)
+    ce = {q: {"loss": f(), "dX": torch.empty((Mc, dc), dtype=torch.bfloat16, device=DEV),
+              "dW": torch.empty((V, dc), dtype=torch.float32, device=DEV),
+              "ws": torch.empty(max(1, (L.softcap_ce_fp8_workspace if q else L.softcap_ce_workspace)(Mc, V, dc, T)),
+                                dtype=torch.uint8, device=DEV)} for q in (False, True)}
+    xs = f(4.0)
+
+    def calls():
+        for c in lin:
+            fm.fp8_linear(c["X"], c["sx"], c["Wt"], c["inv"], c["Y"], x_amax_out=c["xam"], workspace=c["ws"])
+        o = ce[False]
+        fm.softcap_ce_fwd_bwd(Xc, Wc, tg, wts, 15.0, o["loss"], o["dX"], o["dW"], workspace=o["ws"])
+        o = ce[True]
+        fm.softcap_ce_fwd_bwd_fp8(Xc, xs, Wct, cinv, Wc, tg, wts, 15.0, o["loss"], o["dX"], o["dW"],
+                                  workspace=o["ws"])
+
+    def snapshot():
+        s = [bits(c["Y"]) for c in lin] + [c["xam"].cpu().numpy() for c in lin]
+        for q in (False, True):
+            s += [ce[q]["loss"].cpu().numpy(), bits(ce[q]["dX"]), ce[q]["dW"].cpu().numpy()]
+        return s
+
+    inputs = [(c["X"].clone()) for c in lin] + [Xc.clone()]
+
+    def set_inputs(r):
+        # new activations for replay r, written eagerly (a sign flip and a scale by 2^r: exact in bf16)
+        for c, x0 in zip(lin, inputs):
+            c["X"].copy_(x0 * (float(2 ** r) * (-1.0) ** r))
+        Xc.copy_(inputs[-1] * (-1.0) ** r)
+
+    case("fp8_linear and cross-entropy: capture")
+    set_inputs(0)
+    calls()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    torch.cuda.synchronize()
+    for r in range(1, 4):
+        case(f"fp8_linear and cross-entropy: replay {r}")
+        set_inputs(r)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        calls()
+        torch.cuda.synchronize()
+        want = snapshot()
+        for i, (a, b) in enumerate(zip(got, want)):
+            assert np.array_equal(np.asarray(a), np.asarray(b)), (r, i)
+    del g
