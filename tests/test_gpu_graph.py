@@ -174,3 +174,66 @@ def test_linear_and_cross_entropy_captured_in_a_graph():
         for i, (a, b) in enumerate(zip(got, want)):
             assert np.array_equal(np.asarray(a), np.asarray(b)), (r, i)
     del g
+
+
+def test_variant_step_captured_in_a_graph():
+    """The forward with both GEMMs in e4m3 (mlp_relu2_fwd_fp8up, X converted
+    in the launch sequence, max |X| out) and the backward on the e4m3 post copy
+    (mlp_relu2_bwd_fp8post) captured once, replayed three times on new X and
+    dY written between the replays: bit-identical to the eager calls."""
+    fm.lib()
+    L = fm.lib()
+    M, d, h = 2000, 768, 3072
+    ins = synth.mlp_inputs(M, d, h, 98, with_dy=True)
+    X, dY = bf16_dev(ins["X"]), bf16_dev(ins["dY"])
+    X0, dY0 = X.clone(), dY.clone()
+    W1, W2 = bf16_dev(ins["W1"]), bf16_dev(ins["W2"])
+    f = lambda v=0.0: torch.full((1,), v, dtype=torch.float32, device=DEV)
+    W1t = torch.empty((d, h), dtype=torch.uint8, device=DEV)
+    W2t = torch.empty((h, d), dtype=torch.uint8, device=DEV)
+    inv1, inv2 = f(), f()
+    fm.fp8_cast_transpose(W1, W1t, inv_scale_out=inv1)
+    fm.fp8_cast_transpose(W2, W2t, inv_scale_out=inv2)
+    sx, amax_prev, amax_out, scale_out, xam = f(40.0), f(3.0), f(), f(), f()
+    post_q = torch.empty((M, h), dtype=torch.uint8, device=DEV)
+    Y, dX = torch.empty((M, d), dtype=torch.bfloat16, device=DEV), torch.empty((M, d), dtype=torch.bfloat16, device=DEV)
+    dW1 = torch.empty((h, d), dtype=torch.float32, device=DEV)
+    dW2 = torch.empty((d, h), dtype=torch.float32, device=DEV)
+    wsf = torch.empty(max(1, L.mlp_relu2_fwd_fp8up_workspace(M, d, h)), dtype=torch.uint8, device=DEV)
+    wsb = torch.empty(max(1, L.mlp_relu2_bwd_workspace(M, d, h)), dtype=torch.uint8, device=DEV)
+
+    def calls():
+        # post = None: only the e4m3 copy is kept, and the backward reads it
+        fm.mlp_relu2_fwd_fp8up(X, sx, W1t, inv1, W2t, inv2, amax_prev, 2.0, None, post_q, amax_out, scale_out, Y,
+                               x_amax_out=xam, workspace=wsf)
+        fm.mlp_relu2_bwd_fp8post(dY, X, W1, W2, post_q, scale_out, dX, dW1, dW2, workspace=wsb)
+
+    def snapshot():
+        return [bits(Y), post_q.cpu().numpy(), amax_out.cpu().numpy(), scale_out.cpu().numpy(), xam.cpu().numpy(),
+                bits(dX), dW1.cpu().numpy(), dW2.cpu().numpy()]
+
+    def set_inputs(r):
+        X.copy_(X0 * (-1.0) ** r)
+        dY.copy_(dY0 * float(2 ** r))
+
+    case("variant step: capture")
+    set_inputs(0)
+    calls()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    torch.cuda.synchronize()
+    for r in range(1, 4):
+        case(f"variant step: replay {r}")
+        set_inputs(r)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        calls()
+        torch.cuda.synchronize()
+        want = snapshot()
+        for i, (a, b) in enumerate(zip(got, want)):
+            assert np.array_equal(np.asarray(a), np.asarray(b)), (r, i)
+    del g
