@@ -10,8 +10,10 @@ GPT-2-small-shaped tokens (M=49152, d=768, h=3072, margin 2):
   mlp_relu2_bwd (dgrad with sqrt(post), dX, dW1, dW2),
   fp8_cast_transpose_w2 (the W2 cache refresh that follows each update),
 with the measured amax carried to the next step as its amax_prev.
-Inputs are resident in HBM before timing starts; W warm-up steps are not
-timed; K steps are timed with HIP events between two device synchronisations.
+Inputs are resident in HBM before timing starts; the matrix-core probe
+(~20 ms of MFMA work on the workload's operands) runs first, then W warm-up
+steps that are not timed; K steps are timed with HIP events between two
+device synchronisations.
 
 value = 12*M*d*h / t_step in TFLOP/s (the six GEMMs of forward + backward).
 One JSON line goes to stdout; progress goes to stderr.
